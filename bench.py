@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Throughput of one rank's decode-attention share over a paged latent KV head
+on one MI355X, through libsplash_attn's C ABI.
+
+Default workload: the request-owned share of a DP-attention / DOP owner,
+B=16 requests x 4,096 tokens, 128 query heads sharing one latent KV row of
+576 bf16 dims (V = the first 512), page size 64, randomly permuted pages.
+One step = one pass of the whole hot path over one batch:
+  * splash_decode_attn over the batch (split-KV chunks + their merge), and
+  * splash_kv_repack of a seeded half of the batch's requests (all their
+    pages) to a freshly permuted destination pool (the handoff copy).
+Inputs are resident in HBM before timing starts; the timed steps rotate over
+several copies of the inputs (more bytes than the 256 MiB Infinity Cache) so
+that KV reads come from HBM.
+
+Prints ONE JSON line: KV tokens/s over the step, the decode kernel's HBM
+roofline (algorithmic bytes / its measured duration), and the CPU oracle's
+throughput on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+KV_ROW_BYTES = 576 * 2
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="owner",
+                    help="owner | tp | cp | transition | sweep:<owner|tp|cp>:<ctx>")
+    ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-repack", action="store_true", help="time decode attention alone")
+    return ap.parse_args()
+
+
+def build_workload(name):
+    import workloads as W
+    repack = False
+    merge = None
+    splits = 0
+    if name == "owner":
+        case, repack = W.case_owner(), True
+        desc = "request-owned share (DP-attention/DOP owner): B=16 x 4,096 tokens, 128 heads, 576/512 bf16, page 64"
+    elif name == "tp":
+        case, splits = W.case_tp(), 8
+        desc = "head-sliced share (TP rank): B=16 x 16,384 tokens, heads [0,16) of 128, 8 split-KV chunks + merge"
+    elif name == "cp":
+        case, merge = W.case_cp(), W.case_cp_merge()
+        desc = "token-split share (CP rank 3/8): B=16 x 65,536, tokens [24,576, 32,768), 128 heads; merge of 8 sets"
+    elif name == "transition":
+        case, repack = W.case_transition(), True
+        desc = "transition batch: 64 requests log-uniform [512, 65,536], 128 heads; repack of 32 requests"
+    elif name.startswith("sweep:"):
+        _, share, ctx = name.split(":")
+        case = W.sweep_case(share, int(ctx))
+        desc = f"sweep: {share} share, B=16 x {ctx} tokens"
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    return case, desc, repack, merge, splits
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported "
+              "(this build runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import layout_agnostic_latent_amd as sp
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    case, desc, do_repack, merge_case, splits = build_workload(args.workload)
+    if args.no_repack:
+        do_repack = False
+    B, Hs = case.num_reqs, case.num_q_heads
+    kv_tokens = case.kv_tokens()
+    pool_bytes = case.kv_pages.nbytes
+    copies = args.copies or max(2, min(8, math.ceil(1.2e9 / pool_bytes)))
+
+    # ---- inputs, resident in HBM ----
+    q0 = torch.from_numpy(case.q.view(np.int16)).to(dev)
+    kv0 = torch.from_numpy(case.kv_pages.view(np.int16)).to(dev)
+    bt = torch.from_numpy(case.block_table).to(dev)
+    sl = torch.from_numpy(case.seq_lens).to(dev)
+    qs = [q0] + [q0.clone() for _ in range(copies - 1)]
+    kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
+    out = torch.empty((B, Hs, case.d_v), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hs), dtype=torch.float32, device=dev)
+    rep = None
+    if do_repack:
+        rc = W.make_repack_case(case, seed=case.seed + 100)
+        rep = dict(st=torch.from_numpy(rc.src_table).to(dev), dt=torch.from_numpy(rc.dst_table).to(dev),
+                   dst=[torch.empty((rc.dst_num_pages,) + case.kv_pages.shape[1:], dtype=torch.int16, device=dev)
+                        for _ in range(copies)],
+                   pages=rc.dst_num_pages)
+    mrg = None
+    if merge_case is not None:
+        mrg = dict(P=torch.from_numpy(merge_case.partials).to(dev), L=torch.from_numpy(merge_case.lses).to(dev))
+        mrg["out"] = torch.empty(mrg["P"].shape[1:], dtype=torch.float32, device=dev)
+        mrg["lse"] = torch.empty(mrg["P"].shape[1:2], dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        k = i % copies
+        sp.decode_attn(qs[k], kvs[k], bt, sl, case.head_lo, case.head_hi, case.tok_lo, case.tok_hi, out, lse,
+                       d_v=case.d_v, scale=case.scale, num_splits=splits)
+        if mrg is not None:
+            sp.lse_merge(mrg["P"], mrg["L"], mrg["out"], mrg["lse"])
+        if rep is not None:
+            sp.kv_repack(kvs[k], rep["st"], rep["dst"][k], rep["dt"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region 1: the step, nothing else on the stream ----
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- timed region 2: the same steps, each kernel bracketed by HIP events ----
+    sp.profile_start()
+    for i in range(args.steps):
+        step(i)
+    prof = sp.profile_stop()
+    assert sp.device_errors(clear=True) == 0
+
+    dec_n = prof["decode_launches"]
+    dec_us = 1e3 * prof["decode_ms"] / max(1, dec_n)
+    n_split_merges = dec_n if sp.decode_plan(B, case.num_heads, case.d_qk, case.d_v, case.page_size,
+                                             case.max_pages_per_req, case.num_pages, case.scale, case.head_lo,
+                                             case.head_hi, case.tok_lo, case.tok_hi, splits)[0] > 1 else 0
+    merge_us = 1e3 * prof["merge_ms"] / max(1, prof["merge_launches"])
+    repack_us = 1e3 * prof["repack_ms"] / max(1, prof["repack_launches"])
+
+    # algorithmic bytes and flops of one decode-attention call
+    dec_bytes = (kv_tokens * KV_ROW_BYTES + B * Hs * case.d_qk * 2 + B * Hs * case.d_v * 4 + B * Hs * 4
+                 + case.block_table.nbytes + case.seq_lens.nbytes)
+    dec_flops = 2.0 * Hs * (case.d_qk + case.d_v) * kv_tokens
+    achieved = dec_bytes / (dec_us * 1e-6) / 1e9
+    call_us = dec_us + (merge_us if n_split_merges else 0.0)
+
+    parts = {
+        "decode_kernel_us": round(dec_us, 2),
+        "split_merge_kernel_us": round(merge_us, 2) if n_split_merges else None,
+        "decode_call_us": round(call_us, 2),
+        "decode_call_GBps": round(dec_bytes / (call_us * 1e-6) / 1e9, 1),
+        "decode_TFLOPs": round(dec_flops / (dec_us * 1e-6) / 1e12, 1),
+        "decode_mfma_frac": round(dec_flops / (dec_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "decode_kv_tokens_per_s": round(kv_tokens / (dec_us * 1e-6), 1),
+        "algorithmic_bytes_per_decode": int(dec_bytes),
+    }
+    if rep is not None:
+        moved = rep["pages"] * case.kv_pages[0].nbytes
+        parts["repack_kernel_us"] = round(repack_us, 2)
+        parts["repack_bytes_moved"] = int(moved)
+        parts["repack_TBps_rw"] = round(2 * moved / (repack_us * 1e-6) / 1e12, 3)
+        parts["repack_hbm_frac"] = round(2 * moved / (repack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    if mrg is not None:
+        mb = mrg["P"].numel() * 4 + mrg["L"].numel() * 4 + mrg["out"].numel() * 4 + mrg["lse"].numel() * 4
+        parts["lse_merge_us"] = round(merge_us, 2)
+        parts["lse_merge_TBps"] = round(mb / (merge_us * 1e-6) / 1e12, 3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, args.cpu_seconds)
+
+    line = {
+        "metric": "decode-attn KV tokens/s + % of HBM/MFMA roofline, 128-head latent KV, 1 GPU",
+        "value": round(kv_tokens / (ms_per_step * 1e-3), 1),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "num_reqs": B, "kv_tokens": kv_tokens, "heads": Hs, "d_qk": case.d_qk,
+                   "d_v": case.d_v, "page_size": case.page_size, "input_copies": copies,
+                   "step": "decode_attn" + (" + lse_merge" if mrg is not None else "")
+                           + (" + kv_repack(half of the requests)" if rep is not None else "")},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_attn_kernel"},
+        "parts": parts,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(case, budget_s):
+    """The float64 oracle on the host cores, on requests of the same batch, for about budget_s seconds."""
+    import numpy as np
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = cores
+    done_tokens = 0
+    reqs = 0
+    t0 = time.perf_counter()
+    b = 0
+    while True:
+        oracle.decode_attn(case.q, case.kv_pages, case.block_table, case.seq_lens, case.head_lo, case.head_hi,
+                           case.tok_lo, case.tok_hi, case.d_v, case.page_size, case.scale, reqs=[b])
+        lo = max(case.tok_lo, 0)
+        done_tokens += max(0, min(case.tok_hi, int(case.seq_lens[b])) - lo)
+        reqs += 1
+        b = (b + 1) % case.num_reqs
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(done_tokens / el, 1), "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reqs} requests of the same batch (float64 numpy, {done_tokens} KV tokens, {el:.1f} s; "
+                      f"{cores} cores in the affinity mask)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,410 @@
+// Host side of libsplash_attn: argument validation, the launch plan
+// (kernel variant, split-KV chunking), the split-KV workspace, the device
+// error word and the exported C functions declared in include/splash_attn.h.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "splash_attn.h"
+#include "common.h"
+
+// Device error word: an OR of SPLASH_DEVERR_* bits.  Each device holds its
+// own copy; its address is looked up per device.
+__device__ int32_t g_splash_dev_err = 0;
+
+namespace splash {
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kNumCUs = 256;  // MI355X: 256 compute units in 8 XCDs
+
+thread_local std::string t_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  t_last_error = buf;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  return fail(SPLASH_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Launch profiling: events bracketing each kernel while enabled.
+enum LaunchKind { kDecode = 0, kMerge = 1, kRepack = 2 };
+struct TimedLaunch {
+  int kind;
+  hipEvent_t start, stop;
+};
+bool g_profiling = false;
+std::vector<TimedLaunch> g_timed;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (returning hipError_t), bracketed by events when profiling.
+template <typename F>
+hipError_t timed(int kind, hipStream_t stream, F&& launch) {
+  if (!g_profiling) return launch();
+  TimedLaunch t{kind, take_event(), take_event()};
+  if (!t.start || !t.stop) return launch();
+  hipEventRecord(t.start, stream);
+  hipError_t e = launch();
+  hipEventRecord(t.stop, stream);
+  g_timed.push_back(t);
+  return e;
+}
+
+struct DeviceState {
+  int32_t* dev_err = nullptr;  // address of g_splash_dev_err on this device
+  void* workspace = nullptr;
+  size_t workspace_bytes = 0;
+};
+std::mutex g_mu;
+DeviceState g_dev[kMaxDevices];
+
+int current_device(int* dev) {
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (*dev < 0 || *dev >= kMaxDevices) return fail(SPLASH_EHIP, "device index %d out of range", *dev);
+  return SPLASH_OK;
+}
+
+// Caller holds g_mu.
+int device_error_word(int dev, int32_t** out) {
+  DeviceState& st = g_dev[dev];
+  if (!st.dev_err) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_splash_dev_err));
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(g_splash_dev_err)");
+    st.dev_err = (int32_t*)p;
+  }
+  *out = st.dev_err;
+  return SPLASH_OK;
+}
+
+// Caller holds g_mu.  Grows (never shrinks) the split-KV workspace.
+int ensure_workspace(int dev, size_t bytes, void** out) {
+  DeviceState& st = g_dev[dev];
+  if (st.workspace_bytes < bytes) {
+    if (st.workspace) {
+      hipError_t e = hipDeviceSynchronize();  // kernels in flight may still use the old buffer
+      if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+      e = hipFree(st.workspace);
+      st.workspace = nullptr;
+      st.workspace_bytes = 0;
+      if (e != hipSuccess) return fail_hip(e, "hipFree(workspace)");
+    }
+    const size_t grown = bytes + bytes / 4;
+    hipError_t e = hipMalloc(&st.workspace, grown);
+    if (e != hipSuccess) {
+      st.workspace = nullptr;
+      return fail_hip(e, "hipMalloc(split-KV workspace)");
+    }
+    st.workspace_bytes = grown;
+  }
+  *out = st.workspace;
+  return SPLASH_OK;
+}
+
+int page_shift_of(int ps) {
+  for (int s = 4; s <= 8; ++s)
+    if (ps == (1 << s)) return s;
+  return -1;
+}
+
+struct Plan {
+  DecodeVariant variant;
+  int head_groups;      // workgroups along the heads
+  int heads_per_group;  // 32 * wh
+  int grid_splits;      // blockIdx.x extent
+  int fixed_splits;     // > 0: every request cut into this many chunks
+  int chunk_tiles;      // otherwise: 32-token tiles per chunk
+  int64_t workspace_bytes;
+};
+
+int validate_decode(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t tok_lo, int32_t tok_hi) {
+  if (!d) return fail(SPLASH_EINVAL, "desc is NULL");
+  if (d->num_reqs < 0) return fail(SPLASH_EINVAL, "num_reqs = %d < 0", d->num_reqs);
+  if (d->num_heads <= 0) return fail(SPLASH_EINVAL, "num_heads = %d <= 0", d->num_heads);
+  if (d->max_pages_per_req <= 0) return fail(SPLASH_EINVAL, "max_pages_per_req = %d <= 0", d->max_pages_per_req);
+  if (d->num_pages <= 0) return fail(SPLASH_EINVAL, "num_pages = %d <= 0", d->num_pages);
+  if (d->num_splits < 0) return fail(SPLASH_EINVAL, "num_splits = %d < 0", d->num_splits);
+  if (!(d->scale == d->scale) || d->scale == 1.0f / 0.0f || d->scale == -1.0f / 0.0f)
+    return fail(SPLASH_EINVAL, "scale is not finite");
+  if (head_lo < 0 || head_hi > d->num_heads || head_lo >= head_hi)
+    return fail(SPLASH_EINVAL, "head range [%d, %d) not a non-empty subrange of [0, %d)", head_lo, head_hi,
+                d->num_heads);
+  if (tok_hi < tok_lo) return fail(SPLASH_EINVAL, "tok_hi = %d < tok_lo = %d", tok_hi, tok_lo);
+  if (!((d->d_qk == 576 && d->d_v == 512) || (d->d_qk == 80 && d->d_v == 64)))
+    return fail(SPLASH_EUNSUPPORTED, "(d_qk, d_v) = (%d, %d) not built; supported: (576, 512), (80, 64)", d->d_qk,
+                d->d_v);
+  if (page_shift_of(d->page_size) < 0)
+    return fail(SPLASH_EUNSUPPORTED, "page_size = %d not in {16, 32, 64, 128, 256}", d->page_size);
+  if ((int64_t)d->max_pages_per_req * d->page_size > (int64_t)1 << 30)
+    return fail(SPLASH_EINVAL, "max_pages_per_req * page_size exceeds 2^30 tokens");
+  return SPLASH_OK;
+}
+
+int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t tok_lo, int32_t tok_hi, Plan* p) {
+  int rc = validate_decode(d, head_lo, head_hi, tok_lo, tok_hi);
+  if (rc) return rc;
+  const int hs = head_hi - head_lo;
+  const int wv_max = d->d_v / 32 >= 4 ? 4 : d->d_v / 32;
+  if (hs <= 32) {
+    p->variant = {d->d_qk, d->d_v, 1, wv_max};
+  } else if (hs <= 64 && d->d_v / 32 >= 2 && d->d_qk == 576) {
+    p->variant = {d->d_qk, d->d_v, 2, 2};
+  } else {
+    p->variant = {d->d_qk, d->d_v, 4, 1};
+  }
+  p->heads_per_group = 32 * p->variant.wh;
+  p->head_groups = (hs + p->heads_per_group - 1) / p->heads_per_group;
+
+  // Longest token range any request can have in this share.
+  const int64_t cap = (int64_t)d->max_pages_per_req * d->page_size;
+  const int64_t lo = tok_lo > 0 ? tok_lo : 0;
+  const int64_t hi = tok_hi < cap ? tok_hi : cap;
+  const int64_t range = hi > lo ? hi - lo : 0;
+  const int64_t max_tiles = range > 0 ? (hi + kTileTok - 1) / kTileTok - lo / kTileTok : 0;
+
+  int forced = d->num_splits;
+  if (forced == 0) {
+    const char* env = getenv("SPLASH_NUM_SPLITS");
+    if (env && *env) forced = atoi(env);
+    if (forced < 0) forced = 0;
+  }
+  const int64_t base = (int64_t)d->num_reqs * p->head_groups;
+  if (forced > 0) {
+    p->fixed_splits = forced;
+    p->chunk_tiles = 0;
+    p->grid_splits = forced;
+  } else {
+    // Aim for about one workgroup per CU (each holds ~147 KiB of LDS), with
+    // chunks of 4..32 tiles (128..1024 tokens).
+    int64_t want = base > 0 ? (kNumCUs + base - 1) / base : 1;
+    int64_t chunk = want > 0 ? (max_tiles + want - 1) / want : max_tiles;
+    if (chunk < 4) chunk = 4;
+    if (chunk > 32) chunk = 32;
+    if (max_tiles == 0) chunk = 1;
+    p->fixed_splits = 0;
+    p->chunk_tiles = (int)chunk;
+    p->grid_splits = max_tiles > 0 ? (int)((max_tiles + chunk - 1) / chunk) : 1;
+  }
+  if (p->grid_splits < 1) p->grid_splits = 1;
+  if (p->grid_splits > 65535) return fail(SPLASH_EINVAL, "too many split-KV chunks (%d)", p->grid_splits);
+  if (p->grid_splits == 1) {
+    p->workspace_bytes = 0;
+  } else {
+    p->workspace_bytes = (int64_t)p->grid_splits * d->num_reqs * hs * (d->d_v + 1) * (int64_t)sizeof(float);
+  }
+  return SPLASH_OK;
+}
+
+}  // namespace
+}  // namespace splash
+
+using namespace splash;
+
+extern "C" {
+
+const char* splash_last_error(void) { return t_last_error.c_str(); }
+
+int splash_decode_plan(const splash_desc* desc, int32_t head_lo, int32_t head_hi, int32_t tok_lo, int32_t tok_hi,
+                       int32_t* num_splits, int32_t* head_groups, int64_t* workspace_bytes) {
+  Plan p;
+  int rc = make_plan(desc, head_lo, head_hi, tok_lo, tok_hi, &p);
+  if (rc) return rc;
+  if (num_splits) *num_splits = p.grid_splits;
+  if (head_groups) *head_groups = p.head_groups;
+  if (workspace_bytes) *workspace_bytes = p.workspace_bytes;
+  return SPLASH_OK;
+}
+
+int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pages, const int32_t* block_table,
+                       const int32_t* seq_lens, int32_t head_lo, int32_t head_hi, int32_t tok_lo, int32_t tok_hi,
+                       float* out, float* lse, hipStream_t stream) {
+  Plan p;
+  int rc = make_plan(desc, head_lo, head_hi, tok_lo, tok_hi, &p);
+  if (rc) return rc;
+  if (!q || !kv_pages || !block_table || !seq_lens || !out)
+    return fail(SPLASH_EINVAL, "null tensor pointer (q, kv_pages, block_table, seq_lens and out are required)");
+  if ((((uintptr_t)q) & 15) || (((uintptr_t)kv_pages) & 15) || (((uintptr_t)out) & 15))
+    return fail(SPLASH_EINVAL, "q, kv_pages and out must be 16-byte aligned");
+  if (desc->num_reqs == 0) return SPLASH_OK;
+  const int hs = head_hi - head_lo;
+
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  int32_t* dev_err;
+  if ((rc = device_error_word(dev, &dev_err))) return rc;
+
+  DecodeArgs a;
+  a.q = (const uint16_t*)q;
+  a.kv = (const uint16_t*)kv_pages;
+  a.bt = block_table;
+  a.seq_lens = seq_lens;
+  a.dev_err = dev_err;
+  a.q_req_stride = (int64_t)desc->num_heads * desc->d_qk;
+  a.page_stride = (int64_t)desc->page_size * desc->d_qk;
+  a.max_pages = desc->max_pages_per_req;
+  a.num_pages = desc->num_pages;
+  a.page_shift = page_shift_of(desc->page_size);
+  a.head_lo = head_lo;
+  a.n_heads = hs;
+  a.tok_lo = tok_lo;
+  a.tok_hi = tok_hi;
+  a.fixed_splits = p.fixed_splits;
+  a.chunk_tiles = p.chunk_tiles;
+  a.scale_log2 = desc->scale * 1.4426950408889634f;
+
+  const dim3 grid(p.grid_splits, desc->num_reqs, p.head_groups);
+  if (p.grid_splits == 1) {
+    a.out = out;
+    a.lse = lse;
+    a.out_split_stride = 0;
+    a.lse_split_stride = 0;
+    hipError_t e = timed(kDecode, stream, [&] { return launch_decode(p.variant, grid, a, stream); });
+    if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
+    return SPLASH_OK;
+  }
+  void* ws;
+  if ((rc = ensure_workspace(dev, (size_t)p.workspace_bytes, &ws))) return rc;
+  const int64_t rows = (int64_t)desc->num_reqs * hs;
+  float* part_o = (float*)ws;
+  float* part_l = part_o + (int64_t)p.grid_splits * rows * desc->d_v;
+  a.out = part_o;
+  a.lse = part_l;
+  a.out_split_stride = rows * desc->d_v;
+  a.lse_split_stride = rows;
+  hipError_t e = timed(kDecode, stream, [&] { return launch_decode(p.variant, grid, a, stream); });
+  if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
+  e = timed(kMerge, stream,
+            [&] { return launch_lse_merge(part_o, part_l, p.grid_splits, (int32_t)rows, desc->d_v, out, lse, stream); });
+  if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
+  return SPLASH_OK;
+}
+
+int splash_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows, int32_t d_v,
+                     float* out, float* lse_out, hipStream_t stream) {
+  if (!partials || !lses || !out) return fail(SPLASH_EINVAL, "null tensor pointer (partials, lses, out)");
+  if (n_parts < 1) return fail(SPLASH_EINVAL, "n_parts = %d < 1", n_parts);
+  if (rows < 0) return fail(SPLASH_EINVAL, "rows = %d < 0", rows);
+  if (d_v < 1 || (d_v & 3)) return fail(SPLASH_EINVAL, "d_v = %d must be a positive multiple of 4", d_v);
+  if ((((uintptr_t)partials) & 15) || (((uintptr_t)out) & 15))
+    return fail(SPLASH_EINVAL, "partials and out must be 16-byte aligned");
+  hipError_t e;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    e = timed(kMerge, stream, [&] { return launch_lse_merge(partials, lses, n_parts, rows, d_v, out, lse_out, stream); });
+  }
+  if (e != hipSuccess) return fail_hip(e, "lse_merge launch");
+  return SPLASH_OK;
+}
+
+int splash_kv_repack(const void* src_pages, const int32_t* src_table, void* dst_pages, const int32_t* dst_table,
+                     int32_t n_reqs, int32_t max_pages, int64_t page_bytes, int32_t src_num_pages,
+                     int32_t dst_num_pages, int32_t* err_count, hipStream_t stream) {
+  if (!src_pages || !src_table || !dst_pages || !dst_table)
+    return fail(SPLASH_EINVAL, "null pointer (src_pages, src_table, dst_pages, dst_table)");
+  if (n_reqs < 0 || max_pages < 0) return fail(SPLASH_EINVAL, "n_reqs = %d, max_pages = %d", n_reqs, max_pages);
+  if (page_bytes < 1) return fail(SPLASH_EINVAL, "page_bytes = %lld < 1", (long long)page_bytes);
+  if (src_num_pages < 0 || dst_num_pages < 0) return fail(SPLASH_EINVAL, "negative pool size");
+  const int64_t n_pairs = (int64_t)n_reqs * max_pages;
+  if (n_pairs > 0x7fffffff) return fail(SPLASH_EINVAL, "n_reqs * max_pages exceeds 2^31 - 1");
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  int32_t* dev_err;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if ((rc = device_error_word(dev, &dev_err))) return rc;
+  hipError_t e = timed(kRepack, stream, [&] {
+    return launch_kv_repack(src_pages, src_table, dst_pages, dst_table, n_pairs, page_bytes, src_num_pages,
+                            dst_num_pages, err_count, dev_err, stream);
+  });
+  if (e != hipSuccess) return fail_hip(e, "kv_repack launch");
+  return SPLASH_OK;
+}
+
+int splash_device_errors(int32_t* flags, int32_t clear) {
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  int32_t* dev_err;
+  if ((rc = device_error_word(dev, &dev_err))) return rc;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+  int32_t v = 0;
+  e = hipMemcpy(&v, dev_err, sizeof(v), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail_hip(e, "hipMemcpy(device error word)");
+  if (flags) *flags = v;
+  if (clear) {
+    const int32_t zero = 0;
+    e = hipMemcpy(dev_err, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpy(clear device error word)");
+  }
+  return SPLASH_OK;
+}
+
+int splash_release_workspace(void) {
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& st = g_dev[dev];
+  if (st.workspace) {
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+    e = hipFree(st.workspace);
+    st.workspace = nullptr;
+    st.workspace_bytes = 0;
+    if (e != hipSuccess) return fail_hip(e, "hipFree(workspace)");
+  }
+  return SPLASH_OK;
+}
+
+int splash_profile_start(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_profiling = true;
+  return SPLASH_OK;
+}
+
+int splash_profile_stop(splash_profile* out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_profiling = false;
+  splash_profile p;
+  std::memset(&p, 0, sizeof(p));
+  hipError_t e = hipDeviceSynchronize();
+  int rc = SPLASH_OK;
+  if (e != hipSuccess) rc = fail_hip(e, "hipDeviceSynchronize");
+  for (const TimedLaunch& t : g_timed) {
+    float ms = 0.0f;
+    if (rc == SPLASH_OK && hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess) ms = 0.0f;
+    if (t.kind == kDecode) { p.decode_launches++; p.decode_ms += ms; }
+    if (t.kind == kMerge) { p.merge_launches++; p.merge_ms += ms; }
+    if (t.kind == kRepack) { p.repack_launches++; p.repack_ms += ms; }
+    g_event_pool.push_back(t.start);
+    g_event_pool.push_back(t.stop);
+  }
+  g_timed.clear();
+  if (out) *out = p;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal declarations shared by the host layer (api.hip) and the kernel
+// translation units of libsplash_attn.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace splash {
+
+// Arguments of one decode-attention launch (passed by value to the kernel).
+struct DecodeArgs {
+  const uint16_t* q;         // bf16 [B][H][d_qk]
+  const uint16_t* kv;        // bf16 [num_pages][page_size][d_qk]
+  const int32_t* bt;         // int32 [B][max_pages]
+  const int32_t* seq_lens;   // int32 [B]
+  float* out;                // fp32 [splits][B][Hs][d_v] (splits = 1: the caller's output)
+  float* lse;                // fp32 [splits][B][Hs], may be null when splits = 1
+  int32_t* dev_err;          // library device error word
+  int64_t q_req_stride;      // H * d_qk
+  int64_t page_stride;       // page_size * d_qk
+  int64_t out_split_stride;  // B * Hs * d_v
+  int64_t lse_split_stride;  // B * Hs
+  int32_t max_pages;
+  int32_t num_pages;
+  int32_t page_shift;        // log2(page_size)
+  int32_t head_lo;
+  int32_t n_heads;           // Hs = head_hi - head_lo
+  int32_t tok_lo;
+  int32_t tok_hi;
+  int32_t fixed_splits;      // > 0: every request is cut into this many chunks
+  int32_t chunk_tiles;       // fixed_splits == 0: 32-token tiles per chunk
+  float scale_log2;          // scale * log2(e)
+};
+
+// Kernel variants: (d_qk, d_v) with WH waves along the heads (32 heads each)
+// and WV waves along the V columns.
+struct DecodeVariant {
+  int d_qk, d_v, wh, wv;
+};
+
+hipError_t launch_decode(const DecodeVariant& v, dim3 grid, const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows,
+                            int32_t d_v, float* out, float* lse_out, hipStream_t stream);
+
+hipError_t launch_kv_repack(const void* src, const int32_t* src_table, void* dst, const int32_t* dst_table,
+                            int64_t n_pairs, int64_t page_bytes, int32_t src_num_pages,
+                            int32_t dst_num_pages, int32_t* err_count, int32_t* dev_err,
+                            hipStream_t stream);
+
+constexpr int kTileTok = 32;  // tokens per LDS tile of the decode kernel
+
+}  // namespace splash

@@ -1,0 +1,59 @@
+// Merge of partial attention results over disjoint token sets: the combine
+// step of the CP layout (thelatestinai page, Appendix Table 2: each CP rank
+// holds 1/T of every history) and of split-KV within one rank.  Per row:
+//   M = max_p L_p,  L = M + log(sum_p exp(L_p - M)),  O = sum_p exp(L_p - L) O_p.
+// HBM-bound: each partial value is read once, each output written once.
+#include "common.h"
+
+namespace splash {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMergeThreads = 128;
+
+// One workgroup per row; each thread owns float4 columns.  The row's LSEs
+// (n_parts floats) are read by every thread from L1/L2.
+__global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* __restrict__ P,
+                                                                  const float* __restrict__ L,
+                                                                  int32_t n_parts, int32_t rows, int32_t d_v,
+                                                                  float* __restrict__ out,
+                                                                  float* __restrict__ lse_out) {
+  const int64_t row = blockIdx.x;
+  float M = -INFINITY;
+  for (int p = 0; p < n_parts; ++p) M = fmaxf(M, L[(int64_t)p * rows + row]);
+  const int c4n = d_v >> 2;
+  floatx4* orow = (floatx4*)(out + row * d_v);
+  if (M == -INFINITY) {  // no live part (NaN LSEs also end here: fmaxf ignores them)
+    for (int c = threadIdx.x; c < c4n; c += kMergeThreads) orow[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (lse_out && threadIdx.x == 0) lse_out[row] = -INFINITY;
+    return;
+  }
+  float s = 0.0f;
+  for (int p = 0; p < n_parts; ++p) s += __expf(L[(int64_t)p * rows + row] - M);
+  const float lse = M + __logf(s);
+  for (int c = threadIdx.x; c < c4n; c += kMergeThreads) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < n_parts; ++p) {
+      const float lp = L[(int64_t)p * rows + row];
+      if (lp == -INFINITY) continue;  // an empty part: its partial is never read
+      const float w = __expf(lp - lse);
+      const floatx4 v = ((const floatx4*)(P + ((int64_t)p * rows + row) * d_v))[c];
+      acc += w * v;
+    }
+    orow[c] = acc;
+  }
+  if (lse_out && threadIdx.x == 0) lse_out[row] = lse;
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows,
+                            int32_t d_v, float* out, float* lse_out, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(rows), dim3(kMergeThreads), 0, stream, partials, lses, n_parts,
+                     rows, d_v, out, lse_out);
+  return hipGetLastError();
+}
+
+}  // namespace splash

@@ -1,0 +1,125 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, rejects bad host arguments before any HIP call, and plans
+launches (split-KV chunks, head groups, workspace) as a pure host function."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import layout_agnostic_latent_amd as sp
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "splash_attn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(splash_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("splash_decode_attn", "splash_lse_merge", "splash_kv_repack", "splash_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_function(splash):
+    L = splash.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} declared in the header but not exported"
+
+
+def _desc(**kw):
+    d = dict(num_reqs=16, num_heads=128, d_qk=576, d_v=512, page_size=64, max_pages_per_req=64,
+             num_pages=1024, scale=0.0721, num_splits=0)
+    d.update(kw)
+    return sp.make_desc(**d)
+
+
+def _decode_rc(splash, desc, head_lo=0, head_hi=128, tok_lo=0, tok_hi=4096, ptr=0x1000, out=0x2000):
+    L = splash.lib()
+    return L.splash_decode_attn(ctypes.byref(desc), ptr, ptr, ptr, ptr, head_lo, head_hi, tok_lo, tok_hi, out,
+                                None, None)
+
+
+@pytest.mark.parametrize("kw,args,code", [
+    (dict(), dict(head_lo=5, head_hi=5), sp.EINVAL),
+    (dict(), dict(head_lo=-1), sp.EINVAL),
+    (dict(), dict(head_hi=129), sp.EINVAL),
+    (dict(), dict(tok_lo=10, tok_hi=9), sp.EINVAL),
+    (dict(num_heads=0), dict(head_hi=1), sp.EINVAL),
+    (dict(num_reqs=-1), dict(), sp.EINVAL),
+    (dict(num_pages=0), dict(), sp.EINVAL),
+    (dict(max_pages_per_req=0), dict(), sp.EINVAL),
+    (dict(num_splits=-2), dict(), sp.EINVAL),
+    (dict(scale=float("nan")), dict(), sp.EINVAL),
+    (dict(scale=float("inf")), dict(), sp.EINVAL),
+    (dict(d_qk=128, d_v=128), dict(), sp.EUNSUPPORTED),
+    (dict(d_v=256), dict(), sp.EUNSUPPORTED),
+    (dict(page_size=48), dict(), sp.EUNSUPPORTED),
+    (dict(page_size=8), dict(), sp.EUNSUPPORTED),
+    (dict(), dict(ptr=0), sp.EINVAL),
+    (dict(), dict(out=0), sp.EINVAL),
+    (dict(), dict(ptr=0x1008), sp.EINVAL),
+])
+def test_decode_rejects_bad_arguments(splash, kw, args, code):
+    rc = _decode_rc(splash, _desc(**kw), **args)
+    assert rc == code
+    assert splash.lib().splash_last_error().decode()
+
+
+def test_merge_rejects_bad_arguments(splash):
+    L = splash.lib()
+    assert L.splash_lse_merge(0x1000, 0x1000, 0, 4, 512, 0x1000, None, None) == sp.EINVAL
+    assert L.splash_lse_merge(0x1000, 0x1000, 2, -1, 512, 0x1000, None, None) == sp.EINVAL
+    assert L.splash_lse_merge(0x1000, 0x1000, 2, 4, 510, 0x1000, None, None) == sp.EINVAL
+    assert L.splash_lse_merge(None, 0x1000, 2, 4, 512, 0x1000, None, None) == sp.EINVAL
+    assert L.splash_lse_merge(0x1004, 0x1000, 2, 4, 512, 0x1000, None, None) == sp.EINVAL
+
+
+def test_repack_rejects_bad_arguments(splash):
+    L = splash.lib()
+    p = 0x1000
+    assert L.splash_kv_repack(None, p, p, p, 1, 1, 16, 1, 1, None, None) == sp.EINVAL
+    assert L.splash_kv_repack(p, p, p, p, -1, 1, 16, 1, 1, None, None) == sp.EINVAL
+    assert L.splash_kv_repack(p, p, p, p, 1, 1, 0, 1, 1, None, None) == sp.EINVAL
+    assert L.splash_kv_repack(p, p, p, p, 1, 1, 16, -1, 1, None, None) == sp.EINVAL
+    assert L.splash_kv_repack(p, p, p, p, 1 << 20, 1 << 12, 16, 1, 1, None, None) == sp.EINVAL
+
+
+def test_plan_shapes(splash):
+    # request-owned, 128 heads, 4,096 tokens: one head group, split to fill 256 CUs
+    s, g, w = sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096)
+    assert g == 1 and s == 16 and w == 16 * 16 * 128 * 513 * 4
+    # forced splits
+    s, g, w = sp.decode_plan(16, 128, 576, 512, 64, 256, 4096, 0.07, 0, 16, 0, 16384, num_splits=8)
+    assert s == 8 and g == 1 and w == 8 * 16 * 16 * 513 * 4
+    # a 64-head slice uses 32-head x 2 waves groups
+    s, g, _ = sp.decode_plan(2, 128, 576, 512, 64, 8, 16, 0.07, 0, 64, 0, 512)
+    assert g == 1
+    # 100 heads -> one 128-head group; 129..256 heads -> two groups
+    assert sp.decode_plan(2, 256, 576, 512, 64, 8, 16, 0.07, 0, 200, 0, 512)[1] == 2
+    # a tiny share needs no split and no workspace
+    s, g, w = sp.decode_plan(2, 8, 80, 64, 16, 4, 8, 0.1, 0, 8, 0, 64)
+    assert s == 1 and g == 1 and w == 0
+    # chunks never exceed 32 tiles (1,024 tokens), so ragged batches stay balanced
+    s, g, w = sp.decode_plan(256, 128, 576, 512, 64, 64, 20000, 0.07, 0, 128, 0, 4096)
+    assert s == 4
+
+
+def test_plan_env_override(splash, monkeypatch):
+    monkeypatch.setenv("SPLASH_NUM_SPLITS", "5")
+    assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096)[0] == 5
+    # an explicit num_splits in the descriptor wins
+    assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_splits=3)[0] == 3
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The HIP package never imports the CPU oracle (the oracle is test infrastructure)."""
+    pkg = os.path.dirname(sp.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(root, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f

@@ -1,0 +1,369 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle.
+
+Every case uses the seeded generators of ``workloads``.  Bars: attention
+output max abs <= 1e-2 and relative L2 <= 5e-3, LSE abs <= 1e-3; repack
+bit-exact.  Unused KV slots and unreferenced pages hold NaN, so any unmasked
+read shows up as a non-finite output.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import DEV, assert_close, run_decode, run_oracle, to_dev
+
+import layout_agnostic_latent_amd as sp
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _clean_device_errors():
+    sp.device_errors(clear=True)
+    yield
+    assert sp.device_errors(clear=True) == 0, "a kernel raised a device error bit"
+
+
+# ---------------------------------------------------------------------------
+# tiny: B=2, lens 17/64, H=8, d_qk 80, d_v 64, page 16
+# ---------------------------------------------------------------------------
+def test_tiny_full():
+    c = W.case_tiny()
+    _print("case tiny")
+    go, gl = run_decode(c)
+    ro, rl = run_oracle(c)
+    assert_close(go, gl, ro, rl, what="tiny")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 5])
+def test_tiny_forced_splits(splits):
+    c = W.case_tiny()
+    go, gl = run_decode(c, num_splits=splits)
+    ro, rl = run_oracle(c)
+    assert_close(go, gl, ro, rl, what=f"tiny splits={splits}")
+
+
+@pytest.mark.parametrize("heads,toks", [((0, 8), (0, 64)), ((3, 5), (0, 64)), ((0, 8), (5, 40)),
+                                        ((7, 8), (16, 17)), ((0, 8), (-7, 3)), ((1, 6), (17, 64)),
+                                        ((0, 8), (40, 1000)), ((0, 8), (64, 80))])
+def test_tiny_shares(heads, toks):
+    c = W.case_tiny()
+    go, gl = run_decode(c, head_lo=heads[0], head_hi=heads[1], tok_lo=toks[0], tok_hi=toks[1])
+    ro, rl = run_oracle(c, head_lo=heads[0], head_hi=heads[1], tok_lo=toks[0], tok_hi=toks[1])
+    assert_close(go, gl, ro, rl, what=f"tiny heads={heads} toks={toks}")
+
+
+def test_tiny_without_lse():
+    c = W.case_tiny()
+    go, _ = run_decode(c, with_lse=False)
+    ro, rl = run_oracle(c)
+    assert_close(go, None, ro, rl, what="tiny no-lse")
+
+
+# ---------------------------------------------------------------------------
+# request-owned share (DP-attention / DOP owner): B=16 x 4,096, 128 heads
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def owner():
+    c = W.case_owner()
+    return c, to_dev(c), run_oracle(c)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 4, 16])
+def test_owner(owner, splits):
+    c, t, (ro, rl) = owner
+    _print(f"case owner splits={splits}")
+    go, gl = run_decode(c, t, num_splits=splits)
+    err, rel = assert_close(go, gl, ro, rl, what=f"owner splits={splits}")
+    _print(f"  max abs {err:.2e} rel L2 {rel:.2e}")
+
+
+def test_owner_deterministic(owner):
+    c, t, _ = owner
+    a = run_decode(c, t)
+    b = run_decode(c, t)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_owner_request_subsets(owner):
+    """DP-attention / DOP: each owner's call over its own requests equals the batch."""
+    c, t, (ro, rl) = owner
+    T = 3
+    for r in range(T):
+        mine = [b for b in range(c.num_reqs) if b % T == r]
+        idx = torch.tensor(mine, device=DEV)
+        sub = dict(q=t["q"][idx].contiguous(), kv=t["kv"], bt=t["bt"][idx].contiguous(), sl=t["sl"][idx].contiguous())
+        hs = c.num_q_heads
+        out = torch.empty((len(mine), hs, c.d_v), dtype=torch.float32, device=DEV)
+        lse = torch.empty((len(mine), hs), dtype=torch.float32, device=DEV)
+        sp.decode_attn(sub["q"], sub["kv"], sub["bt"], sub["sl"], 0, hs, 0, c.tok_hi, out, lse,
+                       d_v=c.d_v, scale=c.scale)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().double().numpy(), lse.cpu().double().numpy(), ro[mine], rl[mine],
+                     what=f"owner rank {r}")
+
+
+def test_owner_head_slices_concat(owner):
+    """TP: eight 16-head slices, concatenated, equal the all-head result."""
+    c, t, (ro, rl) = owner
+    outs, lses = [], []
+    for r in range(8):
+        go, gl = run_decode(c, t, head_lo=16 * r, head_hi=16 * (r + 1))
+        outs.append(go)
+        lses.append(gl)
+    assert_close(np.concatenate(outs, axis=1), np.concatenate(lses, axis=1), ro, rl, what="owner TP slices")
+
+
+# ---------------------------------------------------------------------------
+# head-sliced share (TP rank): B=16 x 16,384, heads [0,16) of 128
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def tp():
+    c = W.case_tp()
+    return c, to_dev(c), run_oracle(c)
+
+
+def test_tp_one_call_eight_splits(tp):
+    c, t, (ro, rl) = tp
+    _print("case tp splits=8")
+    go, gl = run_decode(c, t, num_splits=8)
+    assert_close(go, gl, ro, rl, what="tp 8 splits")
+
+
+def test_tp_auto_plan(tp):
+    c, t, (ro, rl) = tp
+    go, gl = run_decode(c, t)
+    assert_close(go, gl, ro, rl, what="tp auto")
+
+
+def test_tp_eight_ranges_then_merge(tp):
+    c, t, (ro, rl) = tp
+    s = int(c.seq_lens.max())
+    hs = c.num_q_heads
+    P = torch.empty((8, c.num_reqs * hs, c.d_v), dtype=torch.float32, device=DEV)
+    L = torch.empty((8, c.num_reqs * hs), dtype=torch.float32, device=DEV)
+    for r in range(8):
+        lo, hi = r * s // 8, (r + 1) * s // 8
+        sp.decode_attn(t["q"], t["kv"], t["bt"], t["sl"], c.head_lo, c.head_hi, lo, hi,
+                       P[r].view(c.num_reqs, hs, c.d_v), L[r].view(c.num_reqs, hs), d_v=c.d_v, scale=c.scale)
+    out = torch.empty((c.num_reqs * hs, c.d_v), dtype=torch.float32, device=DEV)
+    lse = torch.empty((c.num_reqs * hs,), dtype=torch.float32, device=DEV)
+    sp.lse_merge(P, L, out, lse)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().double().numpy().reshape(ro.shape), lse.cpu().double().numpy().reshape(rl.shape),
+                 ro, rl, what="tp ranges+merge")
+
+
+# ---------------------------------------------------------------------------
+# token-split share (CP rank 3 of 8): B=16 x 65,536, tokens [24,576, 32,768)
+# ---------------------------------------------------------------------------
+def test_cp_rank_share():
+    c = W.case_cp()   # pages outside the range hold NaN
+    _print("case cp rank share")
+    t = to_dev(c)
+    go, gl = run_decode(c, t)
+    ro, rl = run_oracle(c)
+    assert_close(go, gl, ro, rl, what="cp share")
+    del t
+    torch.cuda.empty_cache()
+
+
+def test_cp_merge_seeded_sets():
+    m = W.case_cp_merge()
+    P = torch.from_numpy(m.partials).to(DEV)
+    L = torch.from_numpy(m.lses).to(DEV)
+    rows, d_v = m.partials.shape[1:]
+    out = torch.empty((rows, d_v), dtype=torch.float32, device=DEV)
+    lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    sp.lse_merge(P, L, out, lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.lse_merge(m.partials, m.lses)
+    assert_close(out.cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl, what="cp merge")
+
+
+def test_cp_eight_ranks_merge_equals_unsplit():
+    """CP: the 8 ranks' partials, merged, equal the unsplit 65,536-token result (2 requests)."""
+    c = W.case_cp(B=2, live_only_in_range=False)
+    t = to_dev(c)
+    s = 65536
+    hs = c.num_q_heads
+    P = torch.empty((8, c.num_reqs * hs, c.d_v), dtype=torch.float32, device=DEV)
+    L = torch.empty((8, c.num_reqs * hs), dtype=torch.float32, device=DEV)
+    for r in range(8):
+        sp.decode_attn(t["q"], t["kv"], t["bt"], t["sl"], 0, hs, r * s // 8, (r + 1) * s // 8,
+                       P[r].view(c.num_reqs, hs, c.d_v), L[r].view(c.num_reqs, hs), d_v=c.d_v, scale=c.scale)
+    out = torch.empty((c.num_reqs * hs, c.d_v), dtype=torch.float32, device=DEV)
+    lse = torch.empty((c.num_reqs * hs,), dtype=torch.float32, device=DEV)
+    sp.lse_merge(P, L, out, lse)
+    torch.cuda.synchronize()
+    ro, rl = run_oracle(c, tok_lo=0, tok_hi=s)
+    assert_close(out.cpu().double().numpy().reshape(ro.shape), lse.cpu().double().numpy().reshape(rl.shape),
+                 ro, rl, what="cp 8 ranks merged")
+    go, gl = run_decode(c, t, tok_lo=0, tok_hi=s)
+    assert_close(go, gl, ro, rl, what="cp unsplit")
+    del t
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# transition batch: 64 ragged requests, 128 heads; repack of 32 requests
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def transition():
+    c = W.case_transition()
+    return c, to_dev(c)
+
+
+def test_transition_decode_sampled(transition):
+    c, t = transition
+    _print("case transition decode")
+    go, gl = run_decode(c, t)
+    lens = c.seq_lens
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 33, 63})
+    ro, rl = run_oracle(c, reqs=pick)
+    assert_close(go, gl, ro, rl, rows=pick, what="transition sampled")
+    # every request: finite, and LSE >= max score lower bound holds trivially via finiteness
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
+
+
+def test_transition_repack_bit_exact(transition):
+    c, t = transition
+    _print("case transition repack")
+    rc = W.make_repack_case(c, seed=5)
+    fill = int(np.int16(np.uint16(rc.dst_fill).view(np.int16)))
+    dst = torch.full((rc.dst_num_pages,) + c.kv_pages.shape[1:], fill, dtype=torch.int16, device=DEV)
+    errs = torch.zeros((1,), dtype=torch.int32, device=DEV)
+    sp.kv_repack(t["kv"], torch.from_numpy(rc.src_table).to(DEV), dst, torch.from_numpy(rc.dst_table).to(DEV), errs)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(np.uint16)
+    want, copied, rejected = oracle.kv_repack(
+        c.kv_pages, rc.src_table, np.full((rc.dst_num_pages,) + c.kv_pages.shape[1:], rc.dst_fill, np.uint16),
+        rc.dst_table)
+    assert int(errs.item()) == rejected == 0
+    assert np.array_equal(got, want), "repack not bit-exact"
+    moved_tokens = int(c.seq_lens[rc.moved_reqs].sum())
+    _print(f"  moved {copied} pages, {moved_tokens} tokens, {copied * c.kv_pages[0].nbytes / 1e9:.3f} GB")
+    # round trip back into a fresh pool at the source positions
+    back = torch.zeros_like(t["kv"])
+    sp.kv_repack(dst, torch.from_numpy(rc.dst_table).to(DEV), back, torch.from_numpy(rc.src_table).to(DEV))
+    torch.cuda.synchronize()
+    moved = rc.src_table[rc.src_table >= 0]
+    assert torch.equal(back[torch.from_numpy(moved).long().to(DEV)], t["kv"][torch.from_numpy(moved).long().to(DEV)])
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+def test_ragged_edges():
+    """Zero-length, one-token, unaligned and page-straddling requests in one batch."""
+    lens = [0, 1, 31, 32, 33, 63, 64, 65, 200, 1000]
+    c = W.make_decode_case("edges", 40, lens, num_heads=128, d_qk=576, d_v=512, page_size=64,
+                           scale=W.LATENT_SCALE, extra_pages=5, max_pages_per_req=20)
+    t = to_dev(c)
+    for toks in [(0, 1 << 30), (5, 70), (31, 33), (64, 65), (-3, 2), (999, 1 << 20), (2000, 3000)]:
+        for splits in (0, 1, 3):
+            go, gl = run_decode(c, t, tok_lo=toks[0], tok_hi=toks[1], num_splits=splits)
+            ro, rl = run_oracle(c, tok_lo=toks[0], tok_hi=toks[1])
+            assert_close(go, gl, ro, rl, what=f"edges toks={toks} splits={splits}")
+
+
+@pytest.mark.parametrize("heads", [(0, 1), (5, 37), (0, 64), (64, 128), (1, 100), (0, 128)])
+def test_head_ranges(heads):
+    c = W.make_decode_case("heads", 41, [300, 77, 1025], num_heads=128, d_qk=576, d_v=512, page_size=64,
+                           scale=W.LATENT_SCALE)
+    go, gl = run_decode(c, head_lo=heads[0], head_hi=heads[1])
+    ro, rl = run_oracle(c, head_lo=heads[0], head_hi=heads[1])
+    assert_close(go, gl, ro, rl, what=f"heads={heads}")
+
+
+@pytest.mark.parametrize("ps", [16, 32, 128, 256])
+def test_other_page_sizes(ps):
+    c = W.make_decode_case("pages", 42, [700, 1, 129, 300], num_heads=40, d_qk=576, d_v=512, page_size=ps,
+                           scale=W.LATENT_SCALE, extra_pages=3)
+    go, gl = run_decode(c)
+    ro, rl = run_oracle(c)
+    assert_close(go, gl, ro, rl, what=f"page_size={ps}")
+
+
+def test_large_scores_rescale():
+    """Scores that grow along the context force the running max to move many times.
+
+    Only the rope dims (not part of V) grow with the token index, so the
+    output stays on the N(0,1) scale the bars are set for."""
+    c = W.make_decode_case("grow", 43, [4096, 2500], num_heads=128, d_qk=576, d_v=512, page_size=64,
+                           scale=W.LATENT_SCALE)
+    for b in range(c.num_reqs):
+        n = int(c.seq_lens[b])
+        for tkn in range(n):
+            p, s = c.block_table[b, tkn // 64], tkn % 64
+            rope = (c.kv_pages[p, s, c.d_v:].astype(np.uint32) << 16).view(np.float32) * (1.0 + tkn / 64.0)
+            c.kv_pages[p, s, c.d_v:] = W.bf16_bits(rope)
+    go, gl = run_decode(c)
+    ro, rl = run_oracle(c)
+    assert_close(go, gl, ro, rl, what="growing scores")
+
+
+def test_bad_page_index_is_flagged_not_faulted():
+    """A block-table entry outside the pool is read as page 0 and raises the device error bit."""
+    c = W.make_decode_case("bad", 44, [130], num_heads=32, d_qk=576, d_v=512, page_size=64,
+                           scale=W.LATENT_SCALE)
+    bt = c.block_table.copy()
+    bt[0, 1] = c.num_pages + 1000
+    c2 = W.DecodeCase(**{**c.__dict__, "block_table": bt})
+    run_decode(c2)
+    assert sp.device_errors(clear=True) & sp.DEVERR_BAD_PAGE
+
+
+def test_merge_edges():
+    rows, d_v = 5, 512
+    P = torch.randn((3, rows, d_v), dtype=torch.float32, device=DEV)
+    L = torch.tensor([[0.0, -math.inf, 1.0, -math.inf, 2.0],
+                      [1.0, -math.inf, -math.inf, -math.inf, 2.0],
+                      [-math.inf, -math.inf, 0.5, 3.0, 2.0]], dtype=torch.float32, device=DEV)
+    P[0, 1] = float("nan")  # a part with LSE -inf is never read
+    out = torch.empty((rows, d_v), dtype=torch.float32, device=DEV)
+    lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    sp.lse_merge(P, L, out, lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.lse_merge(P.cpu().numpy(), L.cpu().numpy())
+    assert_close(out.cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl, what="merge edges")
+    o1 = torch.empty_like(out)
+    sp.lse_merge(P[:1].contiguous(), L[:1].contiguous(), o1)
+    torch.cuda.synchronize()
+    live = torch.isfinite(L[0])
+    assert torch.allclose(o1[live], P[0][live], atol=1e-6, rtol=0)
+
+
+def test_repack_rejects_bad_pairs():
+    src = torch.arange(6 * 4 * 8, dtype=torch.int16, device=DEV).view(6, 4, 8)
+    dst = torch.full((5, 4, 8), -1, dtype=torch.int16, device=DEV)
+    st = torch.tensor([[0, -1, 2, -1, 9, 3]], dtype=torch.int32, device=DEV)
+    dt = torch.tensor([[4, 1, -1, -1, 0, 0]], dtype=torch.int32, device=DEV)
+    errs = torch.zeros((1,), dtype=torch.int32, device=DEV)
+    sp.kv_repack(src, st, dst, dt, errs)
+    torch.cuda.synchronize()
+    want, copied, rejected = oracle.kv_repack(src.cpu().numpy(), st.cpu().numpy(),
+                                              np.full((5, 4, 8), -1, np.int16), dt.cpu().numpy())
+    assert int(errs.item()) == rejected == 3 and copied == 2
+    assert np.array_equal(dst.cpu().numpy(), want)
+    assert sp.device_errors(clear=True) & sp.DEVERR_REPACK_PAIR
+
+
+def test_repack_unaligned_page_bytes():
+    """Pages whose size is not a multiple of 16 bytes take the byte-copy path."""
+    src = torch.randint(-100, 100, (7, 3, 5), dtype=torch.int16, device=DEV)  # 30-byte pages
+    dst = torch.zeros((7, 3, 5), dtype=torch.int16, device=DEV)
+    st = torch.tensor([[6, 0, 3], [1, -1, 2]], dtype=torch.int32, device=DEV)
+    dt = torch.tensor([[0, 6, 1], [2, -1, 3]], dtype=torch.int32, device=DEV)
+    sp.kv_repack(src, st, dst, dt)
+    torch.cuda.synchronize()
+    want, _, _ = oracle.kv_repack(src.cpu().numpy(), st.cpu().numpy(), np.zeros((7, 3, 5), np.int16),
+                                  dt.cpu().numpy())
+    assert np.array_equal(dst.cpu().numpy(), want)
