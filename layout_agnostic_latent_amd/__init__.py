@@ -20,7 +20,9 @@ __all__ = ["LIB_PATH", "SplashError", "lib", "decode_attn", "decode_plan", "lse_
            "device_errors", "release_workspace", "profile_start", "profile_stop", "DEVERR_BAD_PAGE",
            "DEVERR_REPACK_PAIR"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsplash_attn.so")
+# The in-tree build; SPLASH_LIB may name another build of the same library.
+LIB_PATH = os.environ.get("SPLASH_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libsplash_attn.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
 DEVERR_BAD_PAGE, DEVERR_REPACK_PAIR = 1, 2

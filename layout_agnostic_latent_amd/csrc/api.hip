@@ -168,9 +168,17 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
   if (rc) return rc;
   const int hs = head_hi - head_lo;
   const int wv_max = d->d_v / 32 >= 4 ? 4 : d->d_v / 32;
-  if (hs <= 32) {
+  // Heads per workgroup: 32 (4 waves split the V columns), 64 (2 head
+  // groups x 2 column halves) or 128 (4 head groups).  SPLASH_WG_HEADS
+  // overrides the choice (tuning).
+  int wg_heads = hs <= 32 ? 32 : (hs <= 64 ? 64 : 128);
+  if (const char* env = getenv("SPLASH_WG_HEADS")) {
+    const int v = atoi(env);
+    if (v == 32 || v == 64 || v == 128) wg_heads = v;
+  }
+  if (wg_heads == 32) {
     p->variant = {d->d_qk, d->d_v, 1, wv_max};
-  } else if (hs <= 64 && d->d_v / 32 >= 2 && d->d_qk == 576) {
+  } else if (wg_heads == 64 && d->d_v / 32 >= 2 && d->d_qk == 576) {
     p->variant = {d->d_qk, d->d_v, 2, 2};
   } else {
     p->variant = {d->d_qk, d->d_v, 4, 1};
