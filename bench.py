@@ -184,6 +184,8 @@ def main():
         parts["lse_merge_us"] = round(merge_us, 2)
         parts["lse_merge_TBps"] = round(mb / (merge_us * 1e-6) / 1e12, 3)
 
+    traffic = measured_traffic(args.workload, "decode_attn_kernel")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, args.cpu_seconds)
@@ -206,12 +208,30 @@ def main():
                    "step": "decode_attn" + (" + lse_merge" if mrg is not None else "")
                            + (" + kv_repack(half of the requests)" if rep is not None else "")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_attn_kernel"},
         "parts": parts,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(workload, kernel_prefix):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary of this workload (profiles/decode_attn_<workload>.json),
+    or None if there is none or the kernel source changed since it was taken."""
+    from layout_agnostic_latent_amd.rocprof_summary import kernel_source_hash
+    path = os.path.join(ROOT, "profiles", f"decode_attn_{workload.replace(':', '_')}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    for k, r in rec.get("kernels", {}).items():
+        if k.startswith(kernel_prefix) and "traffic_bytes" in r:
+            return r["traffic_bytes"]
+    return None
 
 
 def cpu_baseline(case, budget_s):

@@ -59,15 +59,14 @@ hipEvent_t take_event() {
   return e;
 }
 
-// Runs `launch` (returning hipError_t), bracketed by events when profiling.
+// Runs `launch(start_event, stop_event)`; while profiling, the events are
+// attached to the kernel dispatch itself and kept for splash_profile_stop.
 template <typename F>
-hipError_t timed(int kind, hipStream_t stream, F&& launch) {
-  if (!g_profiling) return launch();
+hipError_t timed(int kind, F&& launch) {
+  if (!g_profiling) return launch(nullptr, nullptr);
   TimedLaunch t{kind, take_event(), take_event()};
-  if (!t.start || !t.stop) return launch();
-  hipEventRecord(t.start, stream);
-  hipError_t e = launch();
-  hipEventRecord(t.stop, stream);
+  if (!t.start || !t.stop) return launch(nullptr, nullptr);
+  hipError_t e = launch(t.start, t.stop);
   g_timed.push_back(t);
   return e;
 }
@@ -290,7 +289,7 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
     a.lse = lse;
     a.out_split_stride = 0;
     a.lse_split_stride = 0;
-    hipError_t e = timed(kDecode, stream, [&] { return launch_decode(p.variant, grid, a, stream); });
+    hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
     if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
     return SPLASH_OK;
   }
@@ -303,10 +302,11 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
   a.lse = part_l;
   a.out_split_stride = rows * desc->d_v;
   a.lse_split_stride = rows;
-  hipError_t e = timed(kDecode, stream, [&] { return launch_decode(p.variant, grid, a, stream); });
+  hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
   if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
-  e = timed(kMerge, stream,
-            [&] { return launch_lse_merge(part_o, part_l, p.grid_splits, (int32_t)rows, desc->d_v, out, lse, stream); });
+  e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
+    return launch_lse_merge(part_o, part_l, p.grid_splits, (int32_t)rows, desc->d_v, out, lse, stream, e0, e1);
+  });
   if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
   return SPLASH_OK;
 }
@@ -322,7 +322,9 @@ int splash_lse_merge(const float* partials, const float* lses, int32_t n_parts, 
   hipError_t e;
   {
     std::lock_guard<std::mutex> lock(g_mu);
-    e = timed(kMerge, stream, [&] { return launch_lse_merge(partials, lses, n_parts, rows, d_v, out, lse_out, stream); });
+    e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
+      return launch_lse_merge(partials, lses, n_parts, rows, d_v, out, lse_out, stream, e0, e1);
+    });
   }
   if (e != hipSuccess) return fail_hip(e, "lse_merge launch");
   return SPLASH_OK;
@@ -343,9 +345,9 @@ int splash_kv_repack(const void* src_pages, const int32_t* src_table, void* dst_
   int32_t* dev_err;
   std::lock_guard<std::mutex> lock(g_mu);
   if ((rc = device_error_word(dev, &dev_err))) return rc;
-  hipError_t e = timed(kRepack, stream, [&] {
+  hipError_t e = timed(kRepack, [&](hipEvent_t e0, hipEvent_t e1) {
     return launch_kv_repack(src_pages, src_table, dst_pages, dst_table, n_pairs, page_bytes, src_num_pages,
-                            dst_num_pages, err_count, dev_err, stream);
+                            dst_num_pages, err_count, dev_err, stream, e0, e1);
   });
   if (e != hipSuccess) return fail_hip(e, "kv_repack launch");
   return SPLASH_OK;

@@ -2,6 +2,7 @@
 // translation units of libsplash_attn.  Not part of the public C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,15 +39,19 @@ struct DecodeVariant {
   int d_qk, d_v, wh, wv;
 };
 
-hipError_t launch_decode(const DecodeVariant& v, dim3 grid, const DecodeArgs& a, hipStream_t stream);
+// Each launcher takes two optional events that, when non-null, record the
+// start and end of the kernel itself (hipExtLaunchKernelGGL), for profiling.
+hipError_t launch_decode(const DecodeVariant& v, dim3 grid, const DecodeArgs& a, hipStream_t stream,
+                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows,
-                            int32_t d_v, float* out, float* lse_out, hipStream_t stream);
+                            int32_t d_v, float* out, float* lse_out, hipStream_t stream,
+                            hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_kv_repack(const void* src, const int32_t* src_table, void* dst, const int32_t* dst_table,
                             int64_t n_pairs, int64_t page_bytes, int32_t src_num_pages,
                             int32_t dst_num_pages, int32_t* err_count, int32_t* dev_err,
-                            hipStream_t stream);
+                            hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 constexpr int kTileTok = 32;  // tokens per LDS tile of the decode kernel
 

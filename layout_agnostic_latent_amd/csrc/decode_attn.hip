@@ -476,22 +476,23 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
 }
 
 template <int D_QK, int D_V, int WH, int WV>
-hipError_t launch_variant(dim3 grid, const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_attn_kernel<D_QK, D_V, WH, WV>), grid, dim3(64 * WH * WV), 0, stream, a);
+hipError_t launch_variant(dim3 grid, const DecodeArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  hipExtLaunchKernelGGL((decode_attn_kernel<D_QK, D_V, WH, WV>), grid, dim3(64 * WH * WV), 0, stream, e0, e1, 0, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeVariant& v, dim3 grid, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeVariant& v, dim3 grid, const DecodeArgs& a, hipStream_t stream, hipEvent_t e0,
+                         hipEvent_t e1) {
   if (v.d_qk == 576 && v.d_v == 512) {
-    if (v.wh == 4 && v.wv == 1) return launch_variant<576, 512, 4, 1>(grid, a, stream);
-    if (v.wh == 2 && v.wv == 2) return launch_variant<576, 512, 2, 2>(grid, a, stream);
-    if (v.wh == 1 && v.wv == 4) return launch_variant<576, 512, 1, 4>(grid, a, stream);
+    if (v.wh == 4 && v.wv == 1) return launch_variant<576, 512, 4, 1>(grid, a, stream, e0, e1);
+    if (v.wh == 2 && v.wv == 2) return launch_variant<576, 512, 2, 2>(grid, a, stream, e0, e1);
+    if (v.wh == 1 && v.wv == 4) return launch_variant<576, 512, 1, 4>(grid, a, stream, e0, e1);
   }
   if (v.d_qk == 80 && v.d_v == 64) {
-    if (v.wh == 4 && v.wv == 1) return launch_variant<80, 64, 4, 1>(grid, a, stream);
-    if (v.wh == 1 && v.wv == 2) return launch_variant<80, 64, 1, 2>(grid, a, stream);
+    if (v.wh == 4 && v.wv == 1) return launch_variant<80, 64, 4, 1>(grid, a, stream, e0, e1);
+    if (v.wh == 1 && v.wv == 2) return launch_variant<80, 64, 1, 2>(grid, a, stream, e0, e1);
   }
   return hipErrorInvalidValue;
 }

@@ -62,11 +62,11 @@ __global__ void __launch_bounds__(kRepackThreads) kv_repack_kernel(const uint8_t
 hipError_t launch_kv_repack(const void* src, const int32_t* src_table, void* dst, const int32_t* dst_table,
                             int64_t n_pairs, int64_t page_bytes, int32_t src_num_pages,
                             int32_t dst_num_pages, int32_t* err_count, int32_t* dev_err,
-                            hipStream_t stream) {
+                            hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   if (n_pairs == 0) return hipSuccess;
-  hipLaunchKernelGGL(kv_repack_kernel, dim3((uint32_t)n_pairs), dim3(kRepackThreads), 0, stream,
-                     (const uint8_t*)src, src_table, (uint8_t*)dst, dst_table, page_bytes, src_num_pages,
-                     dst_num_pages, err_count, dev_err);
+  hipExtLaunchKernelGGL(kv_repack_kernel, dim3((uint32_t)n_pairs), dim3(kRepackThreads), 0, stream, e0, e1, 0,
+                        (const uint8_t*)src, src_table, (uint8_t*)dst, dst_table, page_bytes, src_num_pages,
+                        dst_num_pages, err_count, dev_err);
   return hipGetLastError();
 }
 

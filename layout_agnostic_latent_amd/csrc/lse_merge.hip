@@ -11,6 +11,7 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMergeThreads = 128;
+constexpr int kBatch = 8;  // partial rows loaded before they are combined
 
 // One workgroup per row; each thread owns float4 columns.  The row's LSEs
 // (n_parts floats) are read by every thread from L1/L2.
@@ -34,12 +35,23 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
   const float lse = M + __logf(s);
   for (int c = threadIdx.x; c < c4n; c += kMergeThreads) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < n_parts; ++p) {
-      const float lp = L[(int64_t)p * rows + row];
-      if (lp == -INFINITY) continue;  // an empty part: its partial is never read
-      const float w = __expf(lp - lse);
-      const floatx4 v = ((const floatx4*)(P + ((int64_t)p * rows + row) * d_v))[c];
-      acc += w * v;
+    // kBatch parts' loads in flight at once; empty parts load nothing
+    for (int p0 = 0; p0 < n_parts; p0 += kBatch) {
+      floatx4 v[kBatch];
+      float w[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int p = p0 + u;
+        const float lp = p < n_parts ? L[(int64_t)p * rows + row] : -INFINITY;
+        w[u] = 0.0f;
+        v[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (lp != -INFINITY) {
+          w[u] = __expf(lp - lse);
+          v[u] = ((const floatx4*)(P + ((int64_t)p * rows + row) * d_v))[c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) acc += w[u] * v[u];
     }
     orow[c] = acc;
   }
@@ -49,10 +61,11 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
 }  // namespace
 
 hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows,
-                            int32_t d_v, float* out, float* lse_out, hipStream_t stream) {
+                            int32_t d_v, float* out, float* lse_out, hipStream_t stream, hipEvent_t e0,
+                            hipEvent_t e1) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3(rows), dim3(kMergeThreads), 0, stream, partials, lses, n_parts,
-                     rows, d_v, out, lse_out);
+  hipExtLaunchKernelGGL(lse_merge_kernel, dim3(rows), dim3(kMergeThreads), 0, stream, e0, e1, 0, partials, lses,
+                        n_parts, rows, d_v, out, lse_out);
   return hipGetLastError();
 }
 

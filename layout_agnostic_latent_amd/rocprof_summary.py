@@ -1,0 +1,144 @@
+"""Summarise rocprofv3 output for the kernels of libsplash_attn.
+
+Usage:
+  python -m layout_agnostic_latent_amd.rocprof_summary --name NAME --command CMD \
+      --trace DIR [--fetch DIR --write DIR --calib-kernel KERNEL --calib-read-bytes N \
+      --calib-write-bytes N] [--bench-json FILE]
+
+* --trace DIR: a `rocprofv3 --kernel-trace --stats --output-format csv` output
+  directory; per-kernel call counts and average durations are taken from its
+  kernel trace.
+* --fetch / --write DIR: `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE`
+  output directories (KiB per dispatch).  The counters are scaled by what the
+  same counter reads for a calibration kernel whose bytes are known (the page
+  repack moves a known number of bytes each way).
+
+Writes profiles/NAME.md (the figures, with the commands that produced them)
+and profiles/NAME.json (machine-readable, including a hash of the decode
+kernel's source so that a later build can tell whether the counters still
+describe it).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode_attn.hip", "lse_merge.hip", "kv_repack.hip", "common.h"):
+        with open(os.path.join(PKG, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short(name: str) -> str:
+    for key in ("decode_attn_kernel", "lse_merge_kernel", "kv_repack_kernel"):
+        if key in name:
+            i = name.find("<")
+            j = name.find(">", i)
+            return key + (name[i:j + 1] if key == "decode_attn_kernel" and i >= 0 else "")
+    return name.split("(")[0][:60]
+
+
+def read_trace(d):
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    dur = defaultdict(list)
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            ns = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+            dur[short(row["Kernel_Name"])].append(ns / 1000.0)
+    return dur
+
+
+def read_pmc(d, counter):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    vals = defaultdict(list)
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] == counter:
+                vals[short(row["Kernel_Name"])].append(float(row["Counter_Value"]))
+    return vals
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--name", required=True)
+    ap.add_argument("--command", required=True, action="append", help="command(s) that produced the data")
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--calib-kernel", default="kv_repack_kernel")
+    ap.add_argument("--calib-read-bytes", type=float)
+    ap.add_argument("--calib-write-bytes", type=float)
+    ap.add_argument("--bench-json", help="the bench.py JSON line of the traced run (for context)")
+    args = ap.parse_args()
+
+    dur = read_trace(args.trace)
+    rec = {"name": args.name, "commands": args.command, "kernel_source_hash": kernel_source_hash(), "kernels": {}}
+    for k, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        rec["kernels"][k] = {"calls": len(v), "avg_us": round(statistics.mean(v), 3),
+                             "min_us": round(min(v), 3), "max_us": round(max(v), 3)}
+    if args.fetch and args.write:
+        fetch = read_pmc(args.fetch, "FETCH_SIZE")
+        write = read_pmc(args.write, "WRITE_SIZE")
+        ck = args.calib_kernel
+        f_scale = args.calib_read_bytes / 1024.0 / statistics.mean(fetch[ck])
+        w_scale = args.calib_write_bytes / 1024.0 / statistics.mean(write[ck])
+        rec["calibration"] = {"kernel": ck, "read_bytes": args.calib_read_bytes, "write_bytes": args.calib_write_bytes,
+                              "fetch_kib_raw": statistics.mean(fetch[ck]), "write_kib_raw": statistics.mean(write[ck]),
+                              "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+        for k in rec["kernels"]:
+            if k in fetch and k in write:
+                fb = statistics.mean(fetch[k]) * 1024.0 * f_scale
+                wb = statistics.mean(write[k]) * 1024.0 * w_scale
+                rec["kernels"][k].update({"fetch_kib_raw": statistics.mean(fetch[k]),
+                                          "write_kib_raw": statistics.mean(write[k]),
+                                          "hbm_read_bytes": int(fb), "hbm_write_bytes": int(wb),
+                                          "traffic_bytes": int(fb + wb)})
+    if args.bench_json:
+        with open(args.bench_json) as f:
+            rec["bench"] = json.loads(f.read().strip().splitlines()[-1])
+
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, args.name + ".json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"# {args.name}", "", "Produced by:", ""]
+    lines += [f"    {c}" for c in args.command]
+    lines += ["", f"Kernel source hash: `{rec['kernel_source_hash']}`", "",
+              "| kernel | calls | avg us | min us | max us | HBM read MB | HBM write MB |",
+              "|---|---|---|---|---|---|---|"]
+    for k, r in rec["kernels"].items():
+        rb = r.get("hbm_read_bytes")
+        wb = r.get("hbm_write_bytes")
+        lines.append(f"| `{k}` | {r['calls']} | {r['avg_us']} | {r['min_us']} | {r['max_us']} | "
+                     f"{'' if rb is None else round(rb / 1e6, 2)} | {'' if wb is None else round(wb / 1e6, 2)} |")
+    if "calibration" in rec:
+        c = rec["calibration"]
+        lines += ["", f"Counter calibration on `{c['kernel']}` (known bytes: {c['read_bytes']:.0f} read, "
+                      f"{c['write_bytes']:.0f} written per dispatch): FETCH_SIZE x {c['fetch_scale']}, "
+                      f"WRITE_SIZE x {c['write_scale']}."]
+    if "bench" in rec:
+        b = rec["bench"]
+        lines += ["", "bench.py line of the traced run (timing perturbed by the tracer):", "",
+                  f"    value {b['value']:.4g} {b['unit']}, ms/step {b['ms_per_step']}, "
+                  f"roofline frac {b['roofline']['frac']}"]
+    with open(os.path.join(PROFILES, args.name + ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
