@@ -21,6 +21,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr int kNumCUs = 256;  // MI355X: 256 compute units in 8 XCDs
+constexpr int kMaxChunkTiles = 128;  // longest split-KV chunk (4,096 tokens)
 
 thread_local std::string t_last_error;
 
@@ -204,12 +205,14 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
     p->chunk_tiles = 0;
     p->grid_splits = forced;
   } else {
-    // Aim for about one workgroup per CU (each holds ~147 KiB of LDS), with
-    // chunks of 4..32 tiles (128..1024 tokens).
+    // Aim for one round of about one workgroup per CU (each holds ~147 KiB
+    // of LDS), with chunks of 4..128 tiles (128..4096 tokens): a chunk pays
+    // a fixed cost (Q load, pipeline fill, the store of its partial output),
+    // and every extra chunk adds a partial that the merge reads back.
     int64_t want = base > 0 ? (kNumCUs + base - 1) / base : 1;
     int64_t chunk = want > 0 ? (max_tiles + want - 1) / want : max_tiles;
     if (chunk < 4) chunk = 4;
-    if (chunk > 32) chunk = 32;
+    if (chunk > kMaxChunkTiles) chunk = kMaxChunkTiles;
     if (max_tiles == 0) chunk = 1;
     p->fixed_splits = 0;
     p->chunk_tiles = (int)chunk;
@@ -289,6 +292,7 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
     a.lse = lse;
     a.out_split_stride = 0;
     a.lse_split_stride = 0;
+    a.partial_out = 0;
     hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
     if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
     return SPLASH_OK;
@@ -302,6 +306,7 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
   a.lse = part_l;
   a.out_split_stride = rows * desc->d_v;
   a.lse_split_stride = rows;
+  a.partial_out = 1;
   hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
   if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
   e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {

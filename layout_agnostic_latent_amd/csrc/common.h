@@ -30,6 +30,7 @@ struct DecodeArgs {
   int32_t tok_hi;
   int32_t fixed_splits;      // > 0: every request is cut into this many chunks
   int32_t chunk_tiles;       // fixed_splits == 0: 32-token tiles per chunk
+  int32_t partial_out;       // 1: out/lse are split-KV partials (merged afterwards)
   float scale_log2;          // scale * log2(e)
 };
 

@@ -27,6 +27,8 @@
 //  * O^T[v][head] += V^T[v][tok] . P^T[tok][head] on the same MFMA: P^T comes
 //    straight from the S^T accumulator registers (bf16), V^T from LDS with
 //    ds_read_b64_tr_b16 transposing loads.
+// The loop runs one tile behind on the output: while the matrix cores do the
+// PV products of tile j-1, the VALU computes the softmax of tile j.
 // A chunk writes normalised O and LSE (to the caller's output, or to the
 // split-KV workspace that splash_lse_merge then combines).
 #include <type_traits>
@@ -42,6 +44,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 constexpr int kPageLds = 4096;  // page ids of a chunk staged in LDS (16 KiB)
@@ -95,6 +98,24 @@ __device__ __forceinline__ float max_across_halves(float x) {
 }
 
 
+// Score MFMAs with VGPR accumulators, issued from inline asm: the compiler
+// gives every MFMA of a kernel that uses AGPRs the AGPR form, and the score
+// tile would then have to share the AGPR file with the output accumulators
+// (which fill it).  Accumulating back to back into the same registers needs
+// no wait states; the last MFMA of a chain is followed by 20 wait states so
+// that VALU instructions may read its result.
+__device__ __forceinline__ void mfma_vgpr_first(floatx16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr(floatx16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr_last(floatx16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3"
+               : "+v"(c)
+               : "v"(a), "v"(b));
+}
+
 template <int D_QK, int D_V, int WH, int WV>
 struct Cfg {
   static constexpr int NW = WH * WV;
@@ -110,15 +131,21 @@ struct Cfg {
   static constexpr bool PADDED = (NCH % 8) != 0;     // rows padded to whole slabs
   static constexpr int KS = D_QK / 16;               // K-steps of the score MFMA
   static constexpr int VB = D_V / 32 / WV;           // 32-wide V blocks per wave
+  static constexpr int PB = VB < 8 ? VB : 8;         // V blocks per epilogue pass
+  static constexpr int PITCH = PB * 32 + 4;          // floats per staged output row (+16 B: banks)
+  static constexpr int STAGE_B = NW * 32 * PITCH * 4;  // epilogue staging bytes
+  static constexpr int SMEM_B = NBUF * TILE_B > STAGE_B ? NBUF * TILE_B : STAGE_B;
   static_assert(D_QK % 16 == 0 && D_V % (32 * WV) == 0 && D_V <= D_QK, "shape");
   static_assert(DMA_T % NW == 0, "DMA split");
-  static_assert(NBUF >= 2, "LDS ring");
+  static_assert(NBUF == 4, "LDS ring: two tiles computed, two in flight");
+  static_assert(KS >= 2, "score chain");
+  static_assert(VB % PB == 0, "epilogue passes");
 };
 
 template <int D_QK, int D_V, int WH, int WV>
 __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const DecodeArgs a) {
   using C = Cfg<D_QK, D_V, WH, WV>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::TILE_B];
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_B];
   __shared__ int32_t page_lds[kPageLds];  // this chunk's physical page ids
 
   const int lane = threadIdx.x & 63;
@@ -159,7 +186,9 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   float* lse_ptr = a.lse ? a.lse + split * a.lse_split_stride + (int64_t)b * a.n_heads + hs_safe : nullptr;
 
   if (t_end <= t_begin) {  // empty chunk: O = 0, LSE = -inf
-    if (head_ok) {
+    // A split-KV partial with LSE = -inf is never read by the merge, so only
+    // the LSE is written there; the caller's own output gets the zeros.
+    if (head_ok && !a.partial_out) {
 #pragma unroll
       for (int vb = 0; vb < C::VB; ++vb)
 #pragma unroll
@@ -167,24 +196,13 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
           const int col = (wv * C::VB + vb) * 32 + rq * 8 + g * 4;
           *(floatx4*)(out_row + col) = floatx4{0.f, 0.f, 0.f, 0.f};
         }
-      if (lse_ptr && wv == 0 && g == 0) *lse_ptr = -INFINITY;
     }
+    if (head_ok && lse_ptr && wv == 0 && g == 0) *lse_ptr = -INFINITY;
     return;
   }
   const int ntiles = t_end - t_begin;
 
-  // ---- Q for this wave's 32 heads: B operand of every score MFMA ----
-  bf16x8 qf[C::KS];
-  {
-    const uint16_t* qp = a.q + (int64_t)b * a.q_req_stride + (int64_t)(a.head_lo + hs_safe) * D_QK + 8 * g;
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
-    if (!head_ok) {
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) qf[s] = bf16x8{};
-    }
-  }
-
+  bf16x8 qf[C::KS];  // Q of this wave's 32 heads (loaded after the first DMAs)
   const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   const int ps_mask = (1 << a.page_shift) - 1;
   const bool one_page_per_tile = a.page_shift >= 5;
@@ -196,22 +214,14 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   const int l8 = lane >> 3;
   auto dma_inst = [&](int i) { return C::NW == 4 ? 4 * i + wave : wave * C::DMA_W + i; };
 
-  // The chunk's block-table entries [j0, j1) are staged in LDS once, so that
-  // the tile loop issues no scalar-memory loads: an outstanding scalar load
-  // would make every LDS-read wait in the loop a full drain of the counter
-  // the two share.  Chunks with more pages than fit read the table through
-  // the scalar cache instead.
   const int j0 = (t_begin * kTileTok) >> a.page_shift;
   const int j1 = (mhi - 1) >> a.page_shift;  // last page holding a token of the chunk
+  // The chunk's page ids are staged in LDS (below) unless there are too many.
   const bool pt_lds = j1 - j0 < kPageLds;
-  if (pt_lds) {
-    const int32_t* src = a.bt + (int64_t)b * a.max_pages + j0;
-    for (int j = threadIdx.x; j <= j1 - j0; j += C::NTHREADS) page_lds[j] = src[j];
-    __syncthreads();
-  }
+  bool pt_staged = false;
   // Physical page of token `tok`.
   auto page_of = [&](int tok) -> int {
-    int p = pt_lds ? __builtin_amdgcn_readfirstlane(page_lds[(tok >> a.page_shift) - j0]) : bt_row[tok >> a.page_shift];
+    int p = pt_staged ? __builtin_amdgcn_readfirstlane(page_lds[(tok >> a.page_shift) - j0]) : bt_row[tok >> a.page_shift];
     if ((unsigned)p >= (unsigned)a.num_pages) {
       bad_page = true;
       p = 0;
@@ -296,58 +306,171 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     return vofs[h][vbg & 1] + (uint32_t)((vbg >> 1) * C::SLAB_B + (16 * ks + 8 * h) * 128);
   };
 
-  // One tile: scores, online softmax, output update.  With `with_dma`, the
-  // DMA of a later tile (plan `dp`) is issued between the score MFMAs, so its
-  // issue cost hides behind matrix work.
-  auto compute_tile = [&](int it, auto with_dma, const DmaPlan& dp) {
-    const int t = t_begin + it;
+  // The tile loop is software-pipelined by one tile: iteration j computes the
+  // scores of tile j, then the output update of tile j-1 with the softmax of
+  // tile j interleaved between its MFMAs, so that the exponentials run while
+  // the matrix cores work instead of between the two contractions.
+
+  // ---- S^T = K Q^T (32 tokens x 32 heads) of tile `it` ----
+  // K operands are read PF steps ahead of the MFMA that consumes them.  With
+  // `with_dma`, the DMA of a later tile (plan `dp`) is issued between the
+  // MFMAs, so its issue cost hides behind matrix work.
+  auto qk_tile = [&](int it, auto with_dma, bool do_dma, const DmaPlan& dp, auto&& hook) -> floatx16 {
     const char* tile = smem + (it % C::NBUF) * C::TILE_B;
-
-    // ---- S^T = K Q^T (32 tokens x 32 heads) ----
-    // K operands are read PF steps ahead of the MFMA that consumes them; the
-    // scheduling-group hints keep that interleave (one MFMA, one LDS read).
-    floatx16 sacc = floatx16{};
-    {
-      constexpr int PF = C::KS < 4 ? C::KS : 4;  // K operands in flight
-      bf16x8 kring[PF];
+    constexpr int PF = C::KS < 4 ? C::KS : 4;  // K operands in flight
+    floatx16 sacc;
+    bf16x8 kring[PF];
 #pragma unroll
-      for (int s = 0; s < PF; ++s) kring[s] = *(const bf16x8*)(tile + kofs[s & 3] + C::SLAB_B * (s >> 2));
-      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+    for (int s = 0; s < PF; ++s) kring[s] = *(const bf16x8*)(tile + kofs[s & 3] + C::SLAB_B * (s >> 2));
 #pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        const bf16x8 kf = kring[s % PF];
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (s + PF < C::KS) {
-          kring[s % PF] = *(const bf16x8*)(tile + kofs[(s + PF) & 3] + C::SLAB_B * ((s + PF) >> 2));
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        if constexpr (decltype(with_dma)::value) {
+    for (int s = 0; s < C::KS; ++s) {
+      const bf16x8 kf = kring[s % PF];
+      if (s == 0) mfma_vgpr_first(sacc, kf, qf[0]);
+      else if (s == C::KS - 1) mfma_vgpr_last(sacc, kf, qf[s]);
+      else mfma_vgpr(sacc, kf, qf[s]);
+      if (s + PF < C::KS) kring[s % PF] = *(const bf16x8*)(tile + kofs[(s + PF) & 3] + C::SLAB_B * ((s + PF) >> 2));
+      if constexpr (decltype(with_dma)::value) {
 #pragma unroll
-          for (int i = 0; i < C::DMA_W; ++i)
-            if ((i * C::KS) / C::DMA_W == s) issue_one(dp, i);
-        }
+        for (int i = 0; i < C::DMA_W; ++i)
+          if ((i * C::KS) / C::DMA_W == s && do_dma) issue_one(dp, i);
       }
+      hook(s);
     }
+    return sacc;
+  };
 
-    // ---- scores -> probabilities ----
-    const int tok0 = t * kTileTok;
+  // Tokens of tile `it` outside the chunk's range get score -inf.
+  auto mask_tile = [&](floatx16& s, int it) {
+    const int tok0 = (t_begin + it) * kTileTok;
     const int rlo = max(mlo - tok0, 0);
     const int rhi = min(mhi - tok0, kTileTok);
     if ((rlo > 0) || (rhi < kTileTok)) {
+      // valid rows as a scalar bit mask; element r of this lane is row
+      // 8*(r/4) + (r%4) + 4g, i.e. bit (8*(r/4) + (r%4)) of the mask >> 4g
+      const uint32_t keep = (rhi >= 32 ? 0xffffffffu : ((1u << rhi) - 1u)) & ~((1u << rlo) - 1u);
+      const uint32_t kg = keep >> (4 * g);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * g + (r & 3);
-        if (row < rlo || row >= rhi) sacc[r] = -INFINITY;
+      for (int r = 0; r < 16; ++r)
+        if (!((kg >> (8 * (r >> 2) + (r & 3))) & 1u)) s[r] = -INFINITY;
+    }
+  };
+
+  // Row max of a score tile in log2 units (both halves of the head's column).
+  auto tile_max = [&](const floatx16& s) -> float {
+    float mloc = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[r]);
+    return max_across_halves(mloc) * a.scale_log2;
+  };
+  // p = exp2(s * scale_log2 - m) as bf16 PV operands (tokens 16k .. 16k+15),
+  // with the exact and the rounded sums.
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto probs = [&](const floatx16& s, float m, bf16x8 (&p)[2], float& lsum, float& lrsum) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * k + e], a.scale_log2, -m));
+        p[k][e] = (__bf16)pf;
+        lsum += pf;
+      }
+      // sum of the rounded weights, two per v_dot2_f32_bf16
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pair = {p[k][2 * e], p[k][2 * e + 1]};
+        lrsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lrsum, false);
       }
     }
-    float mloc = sacc[0];
+  };
+
+  // ---- O^T += V^T P^T for tile `it` ----
+  // Two transposing LDS reads feed each MFMA; they run PV_PF MFMAs ahead, and
+  // the first PV_PF are issued by the caller (during the score MFMAs of the
+  // next tile, so that their latency is hidden).  `step(i)` emits a slice of
+  // other work (the next tile's softmax) after MFMA i; the scheduling barrier
+  // keeps each slice between its MFMAs, where the VALU runs while the matrix
+  // core is busy.
+  constexpr int NM = 2 * C::VB;  // PV MFMAs per tile: (k-step, V block)
+  constexpr int PV_PF = NM < 4 ? NM : 4;
+  auto vread = [&](int it, int i) -> bf16x8 {
+    const char* tile = smem + (it % C::NBUF) * C::TILE_B;
+    const int ks = i / C::VB, vb = i % C::VB;
+    const char* v0 = tile + vaddr(0, ks, vb);
+    const char* v1 = tile + vaddr(1, ks, vb);
+    const shortx4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)v0);
+    const shortx4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)v1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto pv_tile = [&](int it, const bf16x8 (&p)[2], bf16x8 (&vring)[PV_PF], auto&& step) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
-    mloc = max_across_halves(mloc) * a.scale_log2;
-    const bool need = mloc > m_run + kRescaleThreshold;
-    if (__any(need)) {
-      const float m_new = need ? mloc : m_run;
+    for (int i = 0; i < NM; ++i) {
+      const int ks = i / C::VB, vb = i % C::VB;
+      const bf16x8 vf = vring[i % PV_PF];
+      oacc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[ks], oacc[vb], 0, 0, 0);
+      if (i + PV_PF < NM) vring[i % PV_PF] = vread(it, i + PV_PF);
+      step(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Hook for the score MFMAs of tile it+1: issue the first PV_PF operand
+  // reads of tile `it` after the last PV_PF score MFMAs.
+  auto vprefetch_hook = [&](int it, bf16x8 (&vring)[PV_PF]) {
+    return [&, it](int sidx) {
+      const int i = sidx - (C::KS - PV_PF);
+      if (i >= 0) vring[i] = vread(it, i);
+    };
+  };
+
+  // One pipelined step: scores of tile `it` are in `s`; the output update of
+  // tile it-1 (weights `pprev`) runs while tile it's softmax is computed:
+  // after MFMAs 0-3 partial row maxima, after MFMA 4 the new running max,
+  // after MFMAs 5-20 one probability each (pairs packed to bf16).
+  auto pv_and_softmax = [&](int it, floatx16& s, bf16x8 (&pprev)[2], bf16x8 (&vring)[PV_PF]) {
+    mask_tile(s, it);
+    float mpart[4];
+    float m_new = m_run;
+    bool need = false;
+    uint32_t pw[2][4];
+    float lsum = 0.0f, lrsum = 0.0f, pf_even = 0.0f;
+    // `pin` ties a value to its slice: pure arithmetic would otherwise be
+    // sunk past the scheduling barriers to the end of the block.
+    auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
+    auto step = [&](int i) {
+      if (i < 4) {
+        mpart[i] = fmaxf(fmaxf(s[4 * i], s[4 * i + 1]), fmaxf(s[4 * i + 2], s[4 * i + 3]));
+        pin(mpart[i]);
+      } else if (i == 4) {
+        const float mloc = max_across_halves(fmaxf(fmaxf(mpart[0], mpart[1]), fmaxf(mpart[2], mpart[3]))) * a.scale_log2;
+        need = mloc > m_run + kRescaleThreshold;
+        m_new = need ? mloc : m_run;
+        pin(m_new);
+      } else if (i < 5 + 16) {
+        const int e = i - 5;
+        float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.scale_log2, -m_new));
+        lsum += pf;
+        pin(lsum);
+        if (e & 1) {
+          const bf16x2 pair = {(__bf16)pf_even, (__bf16)pf};
+          uint32_t w = __builtin_bit_cast(uint32_t, pair);
+          asm volatile("" : "+v"(w));
+          pw[e >> 3][(e & 7) >> 1] = w;
+          lrsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lrsum, false);
+          pin(lrsum);
+        } else {
+          pf_even = pf;
+          pin(pf_even);
+        }
+      }
+    };
+    pv_tile(it - 1, pprev, vring, step);
+#pragma unroll
+    for (int i = 2 * C::VB; i < 5 + 16; ++i) step(i);  // slices beyond the MFMA count
+    const bool any_need = __any(need);
+    if (any_need) {
+      // the PV MFMAs above just wrote the accumulators: let them retire
+      // before the VALU reads them
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
       lr_run *= alpha;
@@ -359,120 +482,149 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
           scale_acc(x, alpha);
           oacc[vb][r] = x;
         }
-      m_run = m_new;
     }
-    // Probabilities of the first 16 tokens (k-step 0 of PV), then the PV
-    // MFMAs of k-step 0 interleaved with the second half of the softmax.
-    bf16x8 pb[2];
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    auto probs = [&](int k) {
+    m_run = m_new;
+    l_run += lsum;
+    lr_run += lrsum;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * k + e], a.scale_log2, -m_run));
-        pb[k][e] = (__bf16)pf;
-        l_run += pf;
-      }
-      // sum of the rounded weights, two per v_dot2_f32_bf16
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2 pair = {pb[k][2 * e], pb[k][2 * e + 1]};
-        lr_run = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lr_run, false);
-      }
-    };
-    probs(0);
-
-    // ---- O^T += V^T P^T ----
-    // Two transposing LDS reads feed each MFMA; they run PV_PF MFMAs ahead.
-    {
-      constexpr int NM = 2 * C::VB;              // MFMAs per tile: (k-step, V block)
-      constexpr int PV_PF = NM < 4 ? NM : 4;
-      auto vread = [&](int i) -> bf16x8 {
-        const int ks = i / C::VB, vb = i % C::VB;
-        const char* v0 = tile + vaddr(0, ks, vb);
-        const char* v1 = tile + vaddr(1, ks, vb);
-        const shortx4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)v0);
-        const shortx4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)v1);
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      bf16x8 vring[PV_PF];
-#pragma unroll
-      for (int i = 0; i < PV_PF; ++i) vring[i] = vread(i);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_PF, 0);
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        const int ks = i / C::VB, vb = i % C::VB;
-        if (i == C::VB) probs(1);  // its exps overlap the k-step 0 MFMAs still in flight
-        const bf16x8 vf = vring[i % PV_PF];
-        oacc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ks], oacc[vb], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i + PV_PF < NM) {
-          vring[i % PV_PF] = vread(i + PV_PF);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-      }
+    for (int k = 0; k < 2; ++k) {
+      const u32x4 w = {pw[k][0], pw[k][1], pw[k][2], pw[k][3]};
+      pprev[k] = __builtin_bit_cast(bf16x8, w);
     }
   };
 
+  const std::integral_constant<bool, true> kDma;
+  const std::integral_constant<bool, false> kNoDma;
+
+  // Prologue: tiles 0 and 1 in flight (two ring slots stay free for the
+  // tiles being computed), issued before anything else the chunk loads.
 #pragma unroll
-  for (int i = 0; i < C::NBUF - 1; ++i)
+  for (int i = 0; i < 2; ++i)
     if (i < ntiles) {
       const DmaPlan d = dma_plan(t_begin + i, i, pages_of(t_begin + i));
 #pragma unroll
       for (int k = 0; k < C::DMA_W; ++k) issue_one(d, k);
     }
+
+  // ---- Q for this wave's 32 heads: B operand of every score MFMA ----
+  {
+    const uint16_t* qp = a.q + (int64_t)b * a.q_req_stride + (int64_t)(a.head_lo + hs_safe) * D_QK + 8 * g;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
+    if (!head_ok) {
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) qf[s] = bf16x8{};
+    }
+  }
+
+  // The chunk's block-table entries [j0, j1] are staged in LDS once, so that
+  // the tile loop issues no scalar-memory loads: an outstanding scalar load
+  // would make every LDS-read wait in the loop a full drain of the counter
+  // the two share.  Chunks with more pages than fit read the table through
+  // the scalar cache instead.  (The first two tiles' DMA, issued above, read
+  // their pages through the scalar cache, so that their HBM latency overlaps
+  // the Q loads and this staging.)
+  if (pt_lds) {
+    const int32_t* src = a.bt + (int64_t)b * a.max_pages + j0;
+    for (int j = threadIdx.x; j <= j1 - j0; j += C::NTHREADS) page_lds[j] = src[j];
+    __syncthreads();
+    pt_staged = true;
+  }
+
   // Make the Q loads complete here, visibly to the compiler, so that it
   // places no vector-memory waits inside the tile loop (those would also
   // drain the KV prefetch, which the counter tracks too).
 #pragma unroll
   for (int s = 0; s < C::KS; ++s) asm volatile("" ::"v"(qf[s]));
 
-  // Main loop: after the barrier that frees its slot, the DMA of tile
-  // it+NBUF-1 is issued between the score MFMAs of tile it, with its page
-  // indices read one iteration ahead.  Two younger tiles stay in flight, so
-  // the wait count is a constant.  The last NBUF-1 tiles issue no DMA.
-  const std::integral_constant<bool, true> kDma;
-  const std::integral_constant<bool, false> kNoDma;
-  const int n_main = ntiles - (C::NBUF - 1);
-  TilePages next = pages_of(t_begin + min(C::NBUF - 1, ntiles - 1));
-  int it = 0;
-  for (; it < n_main; ++it) {
-    wait_vmcnt<(C::NBUF - 2) * C::DMA_W>();
-    __syncthreads();  // every wave's DMA of tile `it` landed; slot of tile it-1 is free
-    const int tn = t_begin + it + C::NBUF - 1;
-    const DmaPlan dp = dma_plan(tn, (it + C::NBUF - 1) % C::NBUF, next);
+  // Iteration 0: scores and softmax of tile 0 (the output is still zero, so
+  // the running max is simply set).  Tile 2's DMA goes into its free slot.
+  bf16x8 pprev[2];
+  TilePages next = pages_of(t_begin + min(2, ntiles - 1));
+  {
+    if (ntiles > 1) wait_vmcnt<C::DMA_W>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    const DmaPlan dp = dma_plan(t_begin + 2, 2 % C::NBUF, next);
+    if (3 < ntiles) next = pages_of(t_begin + 3);
+    floatx16 s = qk_tile(0, kDma, 2 < ntiles, dp, [](int) {});
+    mask_tile(s, 0);
+    m_run = tile_max(s);
+    probs(s, m_run, pprev, l_run, lr_run);
+  }
+
+  // Main loop, iteration j: wait for tile j and barrier (every wave is done
+  // with tile j-2, whose slot takes tile j+2); scores of tile j with the DMA
+  // of tile j+2 interleaved; output update of tile j-1 with tile j's softmax.
+  // One younger tile (j+1) stays in flight across the wait.
+  int it = 1;
+  for (; it + 2 < ntiles; ++it) {
+    wait_vmcnt<C::DMA_W>();
+    __syncthreads();
+    const int tn = t_begin + it + 2;
+    const DmaPlan dp = dma_plan(tn, (it + 2) % C::NBUF, next);
     if (tn + 1 < t_end) next = pages_of(tn + 1);
-    compute_tile(it, kDma, dp);
+    bf16x8 vring[PV_PF];
+    floatx16 s = qk_tile(it, kDma, true, dp, vprefetch_hook(it - 1, vring));
+    pv_and_softmax(it, s, pprev, vring);
   }
   const DmaPlan none{nullptr, nullptr, 0u, 0, 0};
   for (; it < ntiles; ++it) {
-    const int younger = ntiles - 1 - it;  // tiles still in flight behind this one
-    if (younger >= 2) wait_vmcnt<2 * C::DMA_W>();
-    else if (younger == 1) wait_vmcnt<C::DMA_W>();
+    if (it + 1 < ntiles) wait_vmcnt<C::DMA_W>();
     else wait_vmcnt<0>();
     __syncthreads();
-    compute_tile(it, kNoDma, none);
+    bf16x8 vring[PV_PF];
+    floatx16 s = qk_tile(it, kNoDma, false, none, vprefetch_hook(it - 1, vring));
+    pv_and_softmax(it, s, pprev, vring);
   }
-
+  // Output update of the last tile.
+  {
+    bf16x8 vring[PV_PF];
+#pragma unroll
+    for (int i = 0; i < PV_PF; ++i) vring[i] = vread(ntiles - 1, i);
+    pv_tile(ntiles - 1, pprev, vring, [](int) {});
+  }
+  // let the last PV MFMAs retire before the epilogue reads the accumulators
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
   if (bad_page && lane == 0) atomicOr(a.dev_err, 1);
 
   // ---- epilogue: normalise and store ----
+  // The accumulators hold, per lane, 16-byte pieces of 32 different output
+  // rows; stored directly, every instruction would touch 32 rows.  Each wave
+  // instead writes its rows into its own LDS region (the ring is free once
+  // every wave is past its last PV) and stores them back as whole 1-KiB runs.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float lr_tot = lr_run + __shfl_xor(lr_run, 32, 64);
   const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
-  if (head_ok) {
+  __syncthreads();
+  {
+    float* stage = (float*)smem + wave * 32 * C::PITCH;
+    const int head0 = (blockIdx.z * WH + wh) * 32;  // first head of this wave within the share
+    float* out_base = a.out + split * a.out_split_stride + ((int64_t)b * a.n_heads + head0) * D_V;
+    constexpr int ROWF = C::PB * 32;  // staged floats per row and pass
 #pragma unroll
-    for (int vb = 0; vb < C::VB; ++vb)
+    for (int pass = 0; pass < C::VB / C::PB; ++pass) {
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int col = (wv * C::VB + vb) * 32 + rq * 8 + g * 4;
-        floatx4 v;
+      for (int vbl = 0; vbl < C::PB; ++vbl)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = oacc[vb][4 * rq + e] * inv;
-        *(floatx4*)(out_row + col) = v;
+        for (int rq = 0; rq < 4; ++rq) {
+          floatx4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = oacc[pass * C::PB + vbl][4 * rq + e] * inv;
+          *(floatx4*)(stage + n * C::PITCH + vbl * 32 + rq * 8 + 4 * g) = v;
+        }
+      const int col0 = (wv * C::VB + pass * C::PB) * 32;
+#pragma unroll
+      for (int i = 0; i < 32 * ROWF / 256; ++i) {
+        const int e = (i * 64 + lane) * 4;
+        const int row = e / ROWF, col = e % ROWF;
+        const floatx4 v = *(const floatx4*)(stage + row * C::PITCH + col);
+        if (head0 + row < a.n_heads) *(floatx4*)(out_base + (int64_t)row * D_V + col0 + col) = v;
       }
-    if (lse_ptr && wv == 0 && g == 0)
-      *lse_ptr = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    }
   }
+  if (head_ok && lse_ptr && wv == 0 && g == 0)
+    *lse_ptr = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
 }
 
 template <int D_QK, int D_V, int WH, int WV>

@@ -103,9 +103,13 @@ def test_plan_shapes(splash):
     # a tiny share needs no split and no workspace
     s, g, w = sp.decode_plan(2, 8, 80, 64, 16, 4, 8, 0.1, 0, 8, 0, 64)
     assert s == 1 and g == 1 and w == 0
-    # chunks never exceed 32 tiles (1,024 tokens), so ragged batches stay balanced
+    # 256 requests fill the CUs with one chunk each
     s, g, w = sp.decode_plan(256, 128, 576, 512, 64, 64, 20000, 0.07, 0, 128, 0, 4096)
-    assert s == 4
+    assert s == 1 and w == 0
+    # 16 x 65,536 tokens: one round of 256 workgroups, 128-tile (4,096-token) chunks
+    assert sp.decode_plan(16, 128, 576, 512, 64, 1024, 20000, 0.07, 0, 128, 0, 65536)[0] == 16
+    # chunks never exceed 128 tiles: one 1M-token request still gets 256 of them
+    assert sp.decode_plan(1, 128, 576, 512, 64, 16384, 20000, 0.07, 0, 128, 0, 1 << 20)[0] == 256
 
 
 def test_plan_env_override(splash, monkeypatch):
