@@ -137,8 +137,28 @@ struct Plan {
   int grid_splits;      // blockIdx.x extent
   int fixed_splits;     // > 0: every request cut into this many chunks
   int chunk_tiles;      // otherwise: 32-token tiles per chunk
+  // Work-list mode: the decode kernel cuts the chunks from the real lengths;
+  // at most items_max work items (the grid's x extent).
+  bool worklist;
+  int items_max;
+  int target;           // workgroups per head group the chunk length aims at
   int64_t workspace_bytes;
 };
+
+// Work-list workspace layout (byte offsets; every part 256-byte aligned):
+// partial outputs and LSEs per work item, then each request's part list.
+struct WorklistLayout {
+  int64_t part_o, part_l, req_info, total;
+};
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+WorklistLayout worklist_layout(int64_t items, int64_t B, int64_t hs, int64_t d_v) {
+  WorklistLayout w;
+  w.part_o = 0;
+  w.part_l = align256(w.part_o + items * hs * d_v * (int64_t)sizeof(float));
+  w.req_info = align256(w.part_l + items * hs * (int64_t)sizeof(float));
+  w.total = align256(w.req_info + B * 16);
+  return w;
+}
 
 int validate_decode(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t tok_lo, int32_t tok_hi) {
   if (!d) return fail(SPLASH_EINVAL, "desc is NULL");
@@ -220,10 +240,25 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
   }
   if (p->grid_splits < 1) p->grid_splits = 1;
   if (p->grid_splits > 65535) return fail(SPLASH_EINVAL, "too many split-KV chunks (%d)", p->grid_splits);
+  p->worklist = false;
+  p->items_max = 0;
+  p->target = 0;
   if (p->grid_splits == 1) {
     p->workspace_bytes = 0;
-  } else {
+  } else if (forced > 0 || d->num_reqs > kPlanMaxReqs) {
     p->workspace_bytes = (int64_t)p->grid_splits * d->num_reqs * hs * (d->d_v + 1) * (int64_t)sizeof(float);
+  } else {
+    // Requests may be shorter than the table's capacity (ragged batches):
+    // the kernel cuts the chunks from seq_lens.  Full chunks number
+    // at most max(target, B * max_tiles / kMaxChunkTiles), plus one
+    // remainder chunk per request.
+    p->worklist = true;
+    p->target = (int)((kNumCUs + p->head_groups - 1) / p->head_groups);
+    const int64_t by_cap = (int64_t)d->num_reqs * max_tiles / kMaxChunkTiles;
+    const int64_t items = (by_cap > p->target ? by_cap : p->target) + d->num_reqs;
+    if (items > 65535) return fail(SPLASH_EINVAL, "too many split-KV work items (%lld)", (long long)items);
+    p->items_max = (int)items;
+    p->workspace_bytes = worklist_layout(items, d->num_reqs, hs, d->d_v).total;
   }
   return SPLASH_OK;
 }
@@ -267,7 +302,7 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
   int32_t* dev_err;
   if ((rc = device_error_word(dev, &dev_err))) return rc;
 
-  DecodeArgs a;
+  DecodeArgs a{};
   a.q = (const uint16_t*)q;
   a.kv = (const uint16_t*)kv_pages;
   a.bt = block_table;
@@ -300,6 +335,32 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
   void* ws;
   if ((rc = ensure_workspace(dev, (size_t)p.workspace_bytes, &ws))) return rc;
   const int64_t rows = (int64_t)desc->num_reqs * hs;
+  if (p.worklist) {
+    const WorklistLayout w = worklist_layout(p.items_max, desc->num_reqs, hs, desc->d_v);
+    char* base = (char*)ws;
+    float* part_o = (float*)(base + w.part_o);
+    float* part_l = (float*)(base + w.part_l);
+    int4* req_info = (int4*)(base + w.req_info);
+    a.num_reqs = desc->num_reqs;
+    a.plan_target = p.target;
+    a.plan_min_chunk = 4;
+    a.plan_max_chunk = kMaxChunkTiles;
+    a.req_info = req_info;
+    a.out = part_o;
+    a.lse = part_l;
+    a.out_split_stride = (int64_t)hs * desc->d_v;
+    a.lse_split_stride = hs;
+    a.partial_out = 1;
+    const dim3 wgrid(p.items_max, 1, p.head_groups);
+    hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, wgrid, a, stream, e0, e1); });
+    if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
+    e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
+      return launch_lse_merge_segmented(part_o, part_l, req_info, (int32_t)rows, hs, desc->d_v, out, lse, stream, e0,
+                                        e1);
+    });
+    if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
+    return SPLASH_OK;
+  }
   float* part_o = (float*)ws;
   float* part_l = part_o + (int64_t)p.grid_splits * rows * desc->d_v;
   a.out = part_o;

@@ -31,6 +31,20 @@ struct DecodeArgs {
   int32_t fixed_splits;      // > 0: every request is cut into this many chunks
   int32_t chunk_tiles;       // fixed_splits == 0: 32-token tiles per chunk
   int32_t partial_out;       // 1: out/lse are split-KV partials (merged afterwards)
+  // Work-list mode (plan_target > 0): the chunks are cut from the device's
+  // seq_lens inside the kernel.  Every workgroup computes the plan (one
+  // chunk length for the batch so that its total tiles fill about
+  // plan_target workgroups, clamped to [plan_min_chunk, plan_max_chunk];
+  // full chunks numbered first, then one remainder chunk per request) and
+  // takes item blockIdx.x; partial slot s holds rows [s][head][d_v]
+  // (out_split_stride = Hs * d_v).  Workgroup (0, 0, 0) writes, per
+  // request, {first full-chunk slot, full chunks, remainder slot or -1, 0}
+  // to req_info for the merge.
+  int32_t num_reqs;
+  int32_t plan_target;
+  int32_t plan_min_chunk;
+  int32_t plan_max_chunk;
+  int4* req_info;
   float scale_log2;          // scale * log2(e)
 };
 
@@ -48,6 +62,15 @@ hipError_t launch_decode(const DecodeVariant& v, dim3 grid, const DecodeArgs& a,
 hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows,
                             int32_t d_v, float* out, float* lse_out, hipStream_t stream,
                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+
+// Work-list mode handles batches of up to this many requests.
+constexpr int kPlanMaxReqs = 8192;
+
+// Merge of the work-list partials: row (b, h) combines the parts listed in
+// req_info[b] (rows = B * hs).
+hipError_t launch_lse_merge_segmented(const float* partials, const float* lses, const int4* req_info, int32_t rows,
+                                      int32_t hs, int32_t d_v, float* out, float* lse_out, hipStream_t stream,
+                                      hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_kv_repack(const void* src, const int32_t* src_table, void* dst, const int32_t* dst_table,
                             int64_t n_pairs, int64_t page_bytes, int32_t src_num_pages,

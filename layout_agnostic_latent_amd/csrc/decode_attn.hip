@@ -116,6 +116,103 @@ __device__ __forceinline__ void mfma_vgpr_last(floatx16& c, const bf16x8& a, con
                : "v"(a), "v"(b));
 }
 
+// Work-list plan, computed by every workgroup from the device's seq_lens
+// (the host knows only the block table's capacity, which for a ragged batch
+// says little about the work).  Chunk length: the batch's total tiles over
+// plan_target workgroups, clamped to [plan_min_chunk, plan_max_chunk].
+// Items: every request's full chunks, numbered in request order, then one
+// remainder chunk per request that has one.  Returns {request, first tile,
+// end tile, item} for item blockIdx.x, or request -1 past the last item.
+// `scratch` (LDS, >= 64 ints) is free again on return.
+template <int NT>
+__device__ int4 plan_item(const DecodeArgs& a, int32_t* scratch) {
+  constexpr int NWV = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lo = max(a.tok_lo, 0);
+  const int first = lo / kTileTok;
+  const int cap = a.max_pages << a.page_shift;
+  const int per = (a.num_reqs + NT - 1) / NT;  // requests per thread: [tid*per, tid*per + per)
+  auto tiles = [&](int r) -> int {
+    const int h = min(min(a.tok_hi, a.seq_lens[r]), cap);
+    return h > lo ? (h + kTileTok - 1) / kTileTok - first : 0;
+  };
+  long long mine = 0;
+  for (int k = 0; k < per; ++k) {
+    const int r = tid * per + k;
+    if (r < a.num_reqs) mine += tiles(r);
+  }
+  for (int d = 32; d >= 1; d >>= 1) mine += __shfl_xor(mine, d, 64);
+  long long* red = (long long*)scratch;  // [NWV]
+  if (lane == 0) red[wave] = mine;
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < NWV; ++w) total += red[w];
+  const long long full_cap = (long long)a.plan_target * a.plan_max_chunk;
+  const int chunk = total >= full_cap ? a.plan_max_chunk
+                                      : max(a.plan_min_chunk, ((int)total + a.plan_target - 1) / a.plan_target);
+  int nf = 0, nr = 0;
+  for (int k = 0; k < per; ++k) {
+    const int r = tid * per + k;
+    if (r < a.num_reqs) {
+      const int nt = tiles(r);
+      nf += nt / chunk;
+      nr += (nt % chunk) ? 1 : 0;
+    }
+  }
+  int fi = nf, ri = nr;  // inclusive prefix within the wave
+  for (int d = 1; d < 64; d <<= 1) {
+    const int uf = __shfl_up(fi, d, 64), ur = __shfl_up(ri, d, 64);
+    if (lane >= d) {
+      fi += uf;
+      ri += ur;
+    }
+  }
+  int* wsum = scratch + 2 * NWV + 8;  // [NWV][2], clear of red[]
+  if (lane == 63) {
+    wsum[2 * wave] = fi;
+    wsum[2 * wave + 1] = ri;
+  }
+  int* mine_item = scratch + 4 * NWV + 16;  // [4]
+  if (tid == 0) mine_item[0] = -1;
+  __syncthreads();
+  int fb = 0, rb = 0, F = 0, R = 0;
+  for (int w = 0; w < NWV; ++w) {
+    if (w < wave) {
+      fb += wsum[2 * w];
+      rb += wsum[2 * w + 1];
+    }
+    F += wsum[2 * w];
+    R += wsum[2 * w + 1];
+  }
+  int foff = fb + fi - nf;
+  int rnext = F + rb + ri - nr;
+  const int me = blockIdx.x;
+  const bool writer = blockIdx.x == 0 && blockIdx.z == 0;
+  for (int k = 0; k < per; ++k) {
+    const int r = tid * per + k;
+    if (r >= a.num_reqs) break;
+    const int nt = tiles(r);
+    const int nfull = nt / chunk;
+    const int rslot = (nt % chunk) ? rnext++ : -1;
+    if (me >= foff && me < foff + nfull) {
+      const int t0 = first + (me - foff) * chunk;
+      mine_item[0] = r;
+      mine_item[1] = t0;
+      mine_item[2] = t0 + chunk;
+    } else if (me == rslot) {
+      mine_item[0] = r;
+      mine_item[1] = first + nfull * chunk;
+      mine_item[2] = first + nt;
+    }
+    if (writer) a.req_info[r] = make_int4(foff, nfull, rslot, 0);
+    foff += nfull;
+  }
+  __syncthreads();
+  const int4 it = make_int4(mine_item[0], mine_item[1], mine_item[2], me);
+  __syncthreads();
+  return it;
+}
+
 template <int D_QK, int D_V, int WH, int WV>
 struct Cfg {
   static constexpr int NW = WH * WV;
@@ -146,7 +243,7 @@ template <int D_QK, int D_V, int WH, int WV>
 __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const DecodeArgs a) {
   using C = Cfg<D_QK, D_V, WH, WV>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_B];
-  __shared__ int32_t page_lds[kPageLds];  // this chunk's physical page ids
+  __shared__ __attribute__((aligned(16))) int32_t page_lds[kPageLds];  // this chunk's physical page ids
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -155,8 +252,19 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   const int g = lane >> 5;   // k-group of the 32x32x16 operands
   const int n = lane & 31;   // head column (B / C operands), token row (A operand of QK)
 
-  const int b = blockIdx.y;
-  const int split = blockIdx.x;
+  // Work item: request b and its tile range; `split` is the partial-output
+  // slot.  In work-list mode the item comes from the plan below, otherwise
+  // from the grid.
+  int b = blockIdx.y, split = blockIdx.x;
+  int4 item = make_int4(0, 0, 0, 0);
+  const bool worklist = a.plan_target > 0;
+  if (worklist) {
+    item = plan_item<C::NTHREADS>(a, page_lds);
+    if (item.x < 0) return;  // beyond the plan's items
+    b = item.x;
+    split = item.w;
+  }
+  const int b_out = worklist ? 0 : b;  // request term of the output row index
   const int hs = (blockIdx.z * WH + wh) * 32 + n;  // head index within the share
   const bool head_ok = hs < a.n_heads;
   const int hs_safe = head_ok ? hs : 0;
@@ -172,7 +280,10 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   const int lo = max(a.tok_lo, 0);
   const int hi = min(min(a.tok_hi, seq), a.max_pages << a.page_shift);
   int t_begin = 0, t_end = 0;  // absolute tile indices [t_begin, t_end)
-  if (hi > lo) {
+  if (worklist) {
+    t_begin = item.y;
+    t_end = item.z;
+  } else if (hi > lo) {
     const int tf = lo / kTileTok;
     const int nt = (hi + kTileTok - 1) / kTileTok - tf;
     const int chunk = a.fixed_splits > 0 ? (nt + a.fixed_splits - 1) / a.fixed_splits : a.chunk_tiles;
@@ -182,8 +293,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   const int mlo = max(lo, t_begin * kTileTok);
   const int mhi = min(hi, t_end * kTileTok);
 
-  float* out_row = a.out + split * a.out_split_stride + ((int64_t)b * a.n_heads + hs_safe) * D_V;
-  float* lse_ptr = a.lse ? a.lse + split * a.lse_split_stride + (int64_t)b * a.n_heads + hs_safe : nullptr;
+  float* out_row = a.out + split * a.out_split_stride + ((int64_t)b_out * a.n_heads + hs_safe) * D_V;
+  float* lse_ptr = a.lse ? a.lse + split * a.lse_split_stride + (int64_t)b_out * a.n_heads + hs_safe : nullptr;
 
   if (t_end <= t_begin) {  // empty chunk: O = 0, LSE = -inf
     // A split-KV partial with LSE = -inf is never read by the merge, so only
@@ -600,7 +711,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   {
     float* stage = (float*)smem + wave * 32 * C::PITCH;
     const int head0 = (blockIdx.z * WH + wh) * 32;  // first head of this wave within the share
-    float* out_base = a.out + split * a.out_split_stride + ((int64_t)b * a.n_heads + head0) * D_V;
+    float* out_base = a.out + split * a.out_split_stride + ((int64_t)b_out * a.n_heads + head0) * D_V;
     constexpr int ROWF = C::PB * 32;  // staged floats per row and pass
 #pragma unroll
     for (int pass = 0; pass < C::VB / C::PB; ++pass) {

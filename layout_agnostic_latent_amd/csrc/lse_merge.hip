@@ -13,16 +13,40 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kMergeThreads = 128;
 constexpr int kBatch = 8;  // partial rows loaded before they are combined
 
+// Parts of a row: either n_parts uniform parts at p * rows + row (the
+// public merge and grid-mode split-KV), or the parts a device-side plan
+// listed for the row's request (work-list split-KV).
+struct UniformParts {
+  int32_t n_parts, rows;
+  __device__ int count(int64_t) const { return n_parts; }
+  __device__ int64_t index(int64_t row, int p) const { return (int64_t)p * rows + row; }
+};
+struct ListedParts {
+  const int4* req_info;  // {first full-chunk slot, full chunks, remainder slot or -1, 0}
+  int32_t hs;
+  __device__ int4 info(int64_t row) const { return req_info[row / hs]; }
+  __device__ int count(int64_t row) const {
+    const int4 r = info(row);
+    return r.y + (r.z >= 0 ? 1 : 0);
+  }
+  __device__ int64_t index(int64_t row, int p) const {
+    const int4 r = info(row);
+    const int slot = p < r.y ? r.x + p : r.z;
+    return (int64_t)slot * hs + row % hs;
+  }
+};
+
 // One workgroup per row; each thread owns float4 columns.  The row's LSEs
-// (n_parts floats) are read by every thread from L1/L2.
+// (a few floats) are read by every thread from L1/L2.
+template <typename Parts>
 __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* __restrict__ P,
-                                                                  const float* __restrict__ L,
-                                                                  int32_t n_parts, int32_t rows, int32_t d_v,
-                                                                  float* __restrict__ out,
+                                                                  const float* __restrict__ L, Parts parts,
+                                                                  int32_t d_v, float* __restrict__ out,
                                                                   float* __restrict__ lse_out) {
   const int64_t row = blockIdx.x;
+  const int n_parts = parts.count(row);
   float M = -INFINITY;
-  for (int p = 0; p < n_parts; ++p) M = fmaxf(M, L[(int64_t)p * rows + row]);
+  for (int p = 0; p < n_parts; ++p) M = fmaxf(M, L[parts.index(row, p)]);
   const int c4n = d_v >> 2;
   floatx4* orow = (floatx4*)(out + row * d_v);
   if (M == -INFINITY) {  // no live part (NaN LSEs also end here: fmaxf ignores them)
@@ -31,7 +55,7 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
     return;
   }
   float s = 0.0f;
-  for (int p = 0; p < n_parts; ++p) s += __expf(L[(int64_t)p * rows + row] - M);
+  for (int p = 0; p < n_parts; ++p) s += __expf(L[parts.index(row, p)] - M);
   const float lse = M + __logf(s);
   for (int c = threadIdx.x; c < c4n; c += kMergeThreads) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -42,12 +66,13 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int p = p0 + u;
-        const float lp = p < n_parts ? L[(int64_t)p * rows + row] : -INFINITY;
+        const int64_t pi = p < n_parts ? parts.index(row, p) : 0;
+        const float lp = p < n_parts ? L[pi] : -INFINITY;
         w[u] = 0.0f;
         v[u] = floatx4{0.f, 0.f, 0.f, 0.f};
         if (lp != -INFINITY) {
           w[u] = __expf(lp - lse);
-          v[u] = ((const floatx4*)(P + ((int64_t)p * rows + row) * d_v))[c];
+          v[u] = ((const floatx4*)(P + pi * d_v))[c];
         }
       }
 #pragma unroll
@@ -64,8 +89,17 @@ hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_
                             int32_t d_v, float* out, float* lse_out, hipStream_t stream, hipEvent_t e0,
                             hipEvent_t e1) {
   if (rows == 0) return hipSuccess;
-  hipExtLaunchKernelGGL(lse_merge_kernel, dim3(rows), dim3(kMergeThreads), 0, stream, e0, e1, 0, partials, lses,
-                        n_parts, rows, d_v, out, lse_out);
+  hipExtLaunchKernelGGL(lse_merge_kernel<UniformParts>, dim3(rows), dim3(kMergeThreads), 0, stream, e0, e1, 0,
+                        partials, lses, UniformParts{n_parts, rows}, d_v, out, lse_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_merge_segmented(const float* partials, const float* lses, const int4* req_info, int32_t rows,
+                                      int32_t hs, int32_t d_v, float* out, float* lse_out, hipStream_t stream,
+                                      hipEvent_t e0, hipEvent_t e1) {
+  if (rows == 0) return hipSuccess;
+  hipExtLaunchKernelGGL(lse_merge_kernel<ListedParts>, dim3(rows), dim3(kMergeThreads), 0, stream, e0, e1, 0,
+                        partials, lses, ListedParts{req_info, hs}, d_v, out, lse_out);
   return hipGetLastError();
 }
 

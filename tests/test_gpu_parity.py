@@ -261,6 +261,31 @@ def test_transition_repack_bit_exact(transition):
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
+def test_many_ragged_requests():
+    """1,100 requests (more than one planner pass over the batch), lengths 0..400
+    against a 4,800-token capacity, so the chunks are cut on the device."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(0, 401, size=1100)
+    lens[::97] = 0
+    c = W.make_decode_case("many", 41, lens, num_heads=8, d_qk=80, d_v=64, page_size=16,
+                           scale=1.0 / np.sqrt(80.0), std=0.5, max_pages_per_req=300)
+    _print("case many ragged requests")
+    go, gl = run_decode(c)
+    ro, rl = run_oracle(c)
+    assert_close(go, gl, ro, rl, what="many ragged")
+
+
+def test_one_long_request_many_chunks():
+    """A 150,000-token request next to a short and an empty one: about 250
+    device-planned chunks of one request, merged by its own part list."""
+    c = W.make_decode_case("long1", 42, [150000, 777, 0], num_heads=128, d_qk=576, d_v=512, page_size=64,
+                           scale=W.LATENT_SCALE, head_lo=0, head_hi=16)
+    _print("case one long request")
+    go, gl = run_decode(c)
+    ro, rl = run_oracle(c)
+    assert_close(go, gl, ro, rl, what="long request")
+
+
 def test_ragged_edges():
     """Zero-length, one-token, unaligned and page-straddling requests in one batch."""
     lens = [0, 1, 31, 32, 33, 63, 64, 65, 200, 1000]
