@@ -48,6 +48,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 constexpr int kPageLds = 4096;  // page ids of a chunk staged in LDS (16 KiB)
+constexpr int kVPages = 4;      // VGPRs of page ids per lane: chunks of up to 256 pages
 constexpr int kLdsBytes = 160 * 1024 - kPageLds * 4;
 constexpr int kMaxBuf = 4;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = exp2(s - m) stays <= 256
@@ -228,6 +229,12 @@ struct Cfg {
   static constexpr bool PADDED = (NCH % 8) != 0;     // rows padded to whole slabs
   static constexpr int KS = D_QK / 16;               // K-steps of the score MFMA
   static constexpr int VB = D_V / 32 / WV;           // 32-wide V blocks per wave
+  static constexpr int NM = 2 * VB;                  // PV MFMAs per tile: (k-step, V block)
+  static constexpr int KPF = KS < 4 ? KS : 4;        // K operands in flight (score MFMAs)
+  static constexpr int VPF = NM < 4 ? NM : 4;        // V operands in flight (PV MFMAs)
+  // DMA instructions of the next tile issued between the score MFMAs; the
+  // rest go between the PV MFMAs.
+  static constexpr int DMA_QK = DMA_W;
   static constexpr int PB = VB < 8 ? VB : 8;         // V blocks per epilogue pass
   static constexpr int PITCH = PB * 32 + 4;          // floats per staged output row (+16 B: banks)
   static constexpr int STAGE_B = NW * 32 * PITCH * 4;  // epilogue staging bytes
@@ -327,12 +334,35 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
 
   const int j0 = (t_begin * kTileTok) >> a.page_shift;
   const int j1 = (mhi - 1) >> a.page_shift;  // last page holding a token of the chunk
-  // The chunk's page ids are staged in LDS (below) unless there are too many.
+  // Where the tile loop finds the chunk's page ids (set up below, after the
+  // first DMAs): 0 = the block table through the scalar cache, 1 = VGPRs
+  // (page j0 + 64k + l in lane l of vpg[k]; read with v_readlane, no memory
+  // access and no wait in the loop), 2 = LDS (chunks with more pages).
+  const bool pt_vgpr = j1 - j0 < 64 * kVPages;
   const bool pt_lds = j1 - j0 < kPageLds;
-  bool pt_staged = false;
+  int pt_mode = 0;
+  int32_t vpg[kVPages];
   // Physical page of token `tok`.
   auto page_of = [&](int tok) -> int {
-    int p = pt_staged ? __builtin_amdgcn_readfirstlane(page_lds[(tok >> a.page_shift) - j0]) : bt_row[tok >> a.page_shift];
+    const int idx = (tok >> a.page_shift) - j0;
+    int p;
+    if (pt_mode == 1) {
+      // every register read with a constant index (a runtime index would put
+      // vpg in scratch memory), the wave-uniform choice made on the scalars
+      p = __builtin_amdgcn_readlane(vpg[0], idx & 63);
+#pragma unroll
+      for (int k = 1; k < kVPages; ++k) {
+        const int q = __builtin_amdgcn_readlane(vpg[k], idx & 63);
+        p = (idx >> 6) == k ? q : p;
+      }
+    } else {
+      // kept a real branch: memory reads here must not be speculated into
+      // the tile loop's common path, and their wait stays inside it (a wait
+      // at the join would drain the LDS reads of every tile)
+      asm volatile("" ::: "memory");
+      p = pt_mode == 2 ? __builtin_amdgcn_readfirstlane(page_lds[idx]) : bt_row[tok >> a.page_shift];
+      asm volatile("" ::"s"(p));
+    }
     if ((unsigned)p >= (unsigned)a.num_pages) {
       bad_page = true;
       p = 0;
@@ -360,6 +390,10 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     const char* base1;  // + row * ROWG: rows 16..31 on page p1
     uint32_t lds;       // ring slot
     int rlo, rhi1;      // valid rows of the tile
+    // four waves: wave w's instructions all carry rows 8w .. 8w+7 and differ
+    // only by 128 B of chunk, so one lane offset and base serve them all
+    const char* wbase;
+    uint32_t voff;
   };
   auto dma_plan = [&](int t, int slot, TilePages pg) -> DmaPlan {
     const int tok0 = t * kTileTok;
@@ -369,9 +403,22 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     d.lds = smem_base + slot * C::TILE_B;
     d.rlo = max(mlo - tok0, 0);
     d.rhi1 = min(mhi - tok0, kTileTok) - 1;
+    if constexpr (C::NW == 4 && !C::PADDED) {
+      const int R = 8 * wave;
+      const int row = min(max(R + l8, d.rlo), d.rhi1);
+      d.voff = (uint32_t)(row * C::ROWG + 16 * ((lane & 7) ^ (int)row_swizzle(R + l8)));
+      d.wbase = (one_page_per_tile || min(max(R, d.rlo), d.rhi1) < 16) ? d.base0 : d.base1;
+    } else {
+      d.voff = 0;
+      d.wbase = nullptr;
+    }
     return d;
   };
   auto issue_one = [&](const DmaPlan& d, int i) {
+    if constexpr (C::NW == 4 && !C::PADDED) {
+      lds_dma16_s(d.wbase + 128 * i, d.voff, d.lds + (4 * i + wave) * 1024);
+      return;
+    }
     const int nn = dma_inst(i);
     const int R = 8 * (nn % 4);
     const int row = min(max(R + l8, d.rlo), d.rhi1);
@@ -428,7 +475,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // MFMAs, so its issue cost hides behind matrix work.
   auto qk_tile = [&](int it, auto with_dma, bool do_dma, const DmaPlan& dp, auto&& hook) -> floatx16 {
     const char* tile = smem + (it % C::NBUF) * C::TILE_B;
-    constexpr int PF = C::KS < 4 ? C::KS : 4;  // K operands in flight
+    constexpr int PF = C::KPF;
     floatx16 sacc;
     bf16x8 kring[PF];
 #pragma unroll
@@ -442,8 +489,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
       if (s + PF < C::KS) kring[s % PF] = *(const bf16x8*)(tile + kofs[(s + PF) & 3] + C::SLAB_B * ((s + PF) >> 2));
       if constexpr (decltype(with_dma)::value) {
 #pragma unroll
-        for (int i = 0; i < C::DMA_W; ++i)
-          if ((i * C::KS) / C::DMA_W == s && do_dma) issue_one(dp, i);
+        for (int i = 0; i < C::DMA_QK; ++i)
+          if ((i * C::KS) / C::DMA_QK == s && do_dma) issue_one(dp, i);
       }
       hook(s);
     }
@@ -501,8 +548,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // other work (the next tile's softmax) after MFMA i; the scheduling barrier
   // keeps each slice between its MFMAs, where the VALU runs while the matrix
   // core is busy.
-  constexpr int NM = 2 * C::VB;  // PV MFMAs per tile: (k-step, V block)
-  constexpr int PV_PF = NM < 4 ? NM : 4;
+  constexpr int NM = C::NM;
+  constexpr int PV_PF = C::VPF;
   auto vread = [&](int it, int i) -> bf16x8 {
     const char* tile = smem + (it % C::NBUF) * C::TILE_B;
     const int ks = i / C::VB, vb = i % C::VB;
@@ -537,7 +584,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // tile it-1 (weights `pprev`) runs while tile it's softmax is computed:
   // after MFMAs 0-3 partial row maxima, after MFMA 4 the new running max,
   // after MFMAs 5-20 one probability each (pairs packed to bf16).
-  auto pv_and_softmax = [&](int it, floatx16& s, bf16x8 (&pprev)[2], bf16x8 (&vring)[PV_PF]) {
+  auto pv_and_softmax = [&](int it, floatx16& s, bf16x8 (&pprev)[2], bf16x8 (&vring)[PV_PF], auto with_dma,
+                            const DmaPlan& dp) {
     mask_tile(s, it);
     float mpart[4];
     float m_new = m_run;
@@ -548,6 +596,12 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     // sunk past the scheduling barriers to the end of the block.
     auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
     auto step = [&](int i) {
+      if constexpr (decltype(with_dma)::value && C::DMA_QK < C::DMA_W) {
+        constexpr int ND = C::DMA_W - C::DMA_QK;
+#pragma unroll
+        for (int k = 0; k < ND; ++k)
+          if ((k * C::NM) / ND == i) issue_one(dp, C::DMA_QK + k);
+      }
       if (i < 4) {
         mpart[i] = fmaxf(fmaxf(s[4 * i], s[4 * i + 1]), fmaxf(s[4 * i + 2], s[4 * i + 3]));
         pin(mpart[i]);
@@ -628,18 +682,26 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     }
   }
 
-  // The chunk's block-table entries [j0, j1] are staged in LDS once, so that
-  // the tile loop issues no scalar-memory loads: an outstanding scalar load
+  // The chunk's block-table entries [j0, j1] are loaded once, so that the
+  // tile loop issues no scalar-memory loads: an outstanding scalar load
   // would make every LDS-read wait in the loop a full drain of the counter
-  // the two share.  Chunks with more pages than fit read the table through
-  // the scalar cache instead.  (The first two tiles' DMA, issued above, read
-  // their pages through the scalar cache, so that their HBM latency overlaps
-  // the Q loads and this staging.)
-  if (pt_lds) {
+  // the two share.  Up to 64 * kVPages pages go to VGPRs, up to kPageLds to
+  // LDS; longer chunks read the table through the scalar cache.  (The first
+  // two tiles' DMA, issued above, read their pages through the scalar cache,
+  // so that their HBM latency overlaps the Q loads and this setup.)
+  {
     const int32_t* src = a.bt + (int64_t)b * a.max_pages + j0;
-    for (int j = threadIdx.x; j <= j1 - j0; j += C::NTHREADS) page_lds[j] = src[j];
-    __syncthreads();
-    pt_staged = true;
+    if (pt_vgpr) {
+#pragma unroll
+      for (int k = 0; k < kVPages; ++k) vpg[k] = j0 + 64 * k + lane <= j1 ? src[64 * k + lane] : 0;
+#pragma unroll
+      for (int k = 0; k < kVPages; ++k) asm volatile("" ::"v"(vpg[k]));
+      pt_mode = 1;
+    } else if (pt_lds) {
+      for (int j = threadIdx.x; j <= j1 - j0; j += C::NTHREADS) page_lds[j] = src[j];
+      __syncthreads();
+      pt_mode = 2;
+    }
   }
 
   // Make the Q loads complete here, visibly to the compiler, so that it
@@ -659,6 +721,10 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     const DmaPlan dp = dma_plan(t_begin + 2, 2 % C::NBUF, next);
     if (3 < ntiles) next = pages_of(t_begin + 3);
     floatx16 s = qk_tile(0, kDma, 2 < ntiles, dp, [](int) {});
+    if (2 < ntiles) {  // the DMAs that later iterations issue between PV MFMAs
+#pragma unroll
+      for (int k = C::DMA_QK; k < C::DMA_W; ++k) issue_one(dp, k);
+    }
     mask_tile(s, 0);
     m_run = tile_max(s);
     probs(s, m_run, pprev, l_run, lr_run);
@@ -677,16 +743,16 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     if (tn + 1 < t_end) next = pages_of(tn + 1);
     bf16x8 vring[PV_PF];
     floatx16 s = qk_tile(it, kDma, true, dp, vprefetch_hook(it - 1, vring));
-    pv_and_softmax(it, s, pprev, vring);
+    pv_and_softmax(it, s, pprev, vring, kDma, dp);
   }
-  const DmaPlan none{nullptr, nullptr, 0u, 0, 0};
+  const DmaPlan none{nullptr, nullptr, 0u, 0, 0, nullptr, 0u};
   for (; it < ntiles; ++it) {
     if (it + 1 < ntiles) wait_vmcnt<C::DMA_W>();
     else wait_vmcnt<0>();
     __syncthreads();
     bf16x8 vring[PV_PF];
     floatx16 s = qk_tile(it, kNoDma, false, none, vprefetch_hook(it - 1, vring));
-    pv_and_softmax(it, s, pprev, vring);
+    pv_and_softmax(it, s, pprev, vring, kNoDma, none);
   }
   // Output update of the last tile.
   {

@@ -14,25 +14,29 @@ constexpr int kMergeThreads = 128;
 constexpr int kBatch = 8;  // partial rows loaded before they are combined
 
 // Parts of a row: either n_parts uniform parts at p * rows + row (the
-// public merge and grid-mode split-KV), or the parts a device-side plan
-// listed for the row's request (work-list split-KV).
+// public merge and grid-mode split-KV), or the parts the decode kernel
+// listed for the row's request (work-list split-KV).  at(row) resolves the
+// row once; the result maps a part number to the partial row it lives in.
+struct UniformRow {
+  int n;
+  int64_t row, rows;
+  __device__ int64_t index(int p) const { return (int64_t)p * rows + row; }
+};
 struct UniformParts {
   int32_t n_parts, rows;
-  __device__ int count(int64_t) const { return n_parts; }
-  __device__ int64_t index(int64_t row, int p) const { return (int64_t)p * rows + row; }
+  __device__ UniformRow at(int64_t row) const { return {n_parts, row, rows}; }
+};
+struct ListedRow {
+  int n, first, nfull, rem, hs, h;
+  __device__ int64_t index(int p) const { return (int64_t)(p < nfull ? first + p : rem) * hs + h; }
 };
 struct ListedParts {
   const int4* req_info;  // {first full-chunk slot, full chunks, remainder slot or -1, 0}
   int32_t hs;
-  __device__ int4 info(int64_t row) const { return req_info[row / hs]; }
-  __device__ int count(int64_t row) const {
-    const int4 r = info(row);
-    return r.y + (r.z >= 0 ? 1 : 0);
-  }
-  __device__ int64_t index(int64_t row, int p) const {
-    const int4 r = info(row);
-    const int slot = p < r.y ? r.x + p : r.z;
-    return (int64_t)slot * hs + row % hs;
+  __device__ ListedRow at(int64_t row) const {
+    const int r = (int)row;  // rows = B * hs < 2^31
+    const int4 info = req_info[r / hs];
+    return {info.y + (info.z >= 0 ? 1 : 0), info.x, info.y, info.z, hs, r % hs};
   }
 };
 
@@ -44,9 +48,10 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
                                                                   int32_t d_v, float* __restrict__ out,
                                                                   float* __restrict__ lse_out) {
   const int64_t row = blockIdx.x;
-  const int n_parts = parts.count(row);
+  const auto rp = parts.at(row);
+  const int n_parts = rp.n;
   float M = -INFINITY;
-  for (int p = 0; p < n_parts; ++p) M = fmaxf(M, L[parts.index(row, p)]);
+  for (int p = 0; p < n_parts; ++p) M = fmaxf(M, L[rp.index(p)]);
   const int c4n = d_v >> 2;
   floatx4* orow = (floatx4*)(out + row * d_v);
   if (M == -INFINITY) {  // no live part (NaN LSEs also end here: fmaxf ignores them)
@@ -55,7 +60,7 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
     return;
   }
   float s = 0.0f;
-  for (int p = 0; p < n_parts; ++p) s += __expf(L[parts.index(row, p)] - M);
+  for (int p = 0; p < n_parts; ++p) s += __expf(L[rp.index(p)] - M);
   const float lse = M + __logf(s);
   for (int c = threadIdx.x; c < c4n; c += kMergeThreads) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -66,7 +71,7 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int p = p0 + u;
-        const int64_t pi = p < n_parts ? parts.index(row, p) : 0;
+        const int64_t pi = p < n_parts ? rp.index(p) : 0;
         const float lp = p < n_parts ? L[pi] : -INFINITY;
         w[u] = 0.0f;
         v[u] = floatx4{0.f, 0.f, 0.f, 0.f};
