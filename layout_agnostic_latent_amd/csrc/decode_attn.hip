@@ -51,7 +51,8 @@ constexpr int kPageLds = 4096;  // page ids of a chunk staged in LDS (16 KiB)
 constexpr int kVPages = 4;      // VGPRs of page ids per lane: chunks of up to 256 pages
 constexpr int kLdsBytes = 160 * 1024 - kPageLds * 4;
 constexpr int kMaxBuf = 4;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = exp2(s - m) stays <= 256
+constexpr float kRescaleThreshold = 8.0f;
+constexpr int kPlanStep = 22;  // PV MFMA after which the next tile's DMA plan is made (past the softmax slices)  // log2 units: p = exp2(s - m) stays <= 256
 
 // LDS tile layout ("slabs"): the 16-byte chunk c of tile row r lives at
 //   (c / 8) * SLAB_B + r * 128 + ((c % 8) ^ row_swizzle(r)) * 16,
@@ -585,7 +586,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // after MFMAs 0-3 partial row maxima, after MFMA 4 the new running max,
   // after MFMAs 5-20 one probability each (pairs packed to bf16).
   auto pv_and_softmax = [&](int it, floatx16& s, bf16x8 (&pprev)[2], bf16x8 (&vring)[PV_PF], auto with_dma,
-                            const DmaPlan& dp) {
+                            const DmaPlan& dp, auto&& extra) {
     mask_tile(s, it);
     float mpart[4];
     float m_new = m_run;
@@ -596,6 +597,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     // sunk past the scheduling barriers to the end of the block.
     auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
     auto step = [&](int i) {
+      extra(i);
       if constexpr (decltype(with_dma)::value && C::DMA_QK < C::DMA_W) {
         constexpr int ND = C::DMA_W - C::DMA_QK;
 #pragma unroll
@@ -629,8 +631,10 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
       }
     };
     pv_tile(it - 1, pprev, vring, step);
+    // slices beyond the MFMA count (variants with fewer V blocks)
+    constexpr int kSteps = 5 + 16 > kPlanStep + 1 ? 5 + 16 : kPlanStep + 1;
 #pragma unroll
-    for (int i = 2 * C::VB; i < 5 + 16; ++i) step(i);  // slices beyond the MFMA count
+    for (int i = C::NM; i < kSteps; ++i) step(i);
     const bool any_need = __any(need);
     if (any_need) {
       // the PV MFMAs above just wrote the accumulators: let them retire
@@ -713,13 +717,12 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // Iteration 0: scores and softmax of tile 0 (the output is still zero, so
   // the running max is simply set).  Tile 2's DMA goes into its free slot.
   bf16x8 pprev[2];
-  TilePages next = pages_of(t_begin + min(2, ntiles - 1));
+  DmaPlan dp;  // DMA of the tile two ahead of the one being scored
   {
     if (ntiles > 1) wait_vmcnt<C::DMA_W>();
     else wait_vmcnt<0>();
     __syncthreads();
-    const DmaPlan dp = dma_plan(t_begin + 2, 2 % C::NBUF, next);
-    if (3 < ntiles) next = pages_of(t_begin + 3);
+    dp = dma_plan(t_begin + 2, 2 % C::NBUF, pages_of(t_begin + min(2, ntiles - 1)));
     floatx16 s = qk_tile(0, kDma, 2 < ntiles, dp, [](int) {});
     if (2 < ntiles) {  // the DMAs that later iterations issue between PV MFMAs
 #pragma unroll
@@ -728,22 +731,27 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     mask_tile(s, 0);
     m_run = tile_max(s);
     probs(s, m_run, pprev, l_run, lr_run);
+    if (3 < ntiles) dp = dma_plan(t_begin + 3, 3 % C::NBUF, pages_of(t_begin + 3));
   }
 
   // Main loop, iteration j: wait for tile j and barrier (every wave is done
   // with tile j-2, whose slot takes tile j+2); scores of tile j with the DMA
-  // of tile j+2 interleaved; output update of tile j-1 with tile j's softmax.
+  // of tile j+2 interleaved; output update of tile j-1 with tile j's softmax,
+  // and, in the PV MFMAs' slack after the softmax, the page lookups and DMA
+  // plan of tile j+3 (scalar work, off the path into the next scores).
   // One younger tile (j+1) stays in flight across the wait.
   int it = 1;
   for (; it + 2 < ntiles; ++it) {
     wait_vmcnt<C::DMA_W>();
     __syncthreads();
-    const int tn = t_begin + it + 2;
-    const DmaPlan dp = dma_plan(tn, (it + 2) % C::NBUF, next);
-    if (tn + 1 < t_end) next = pages_of(tn + 1);
     bf16x8 vring[PV_PF];
     floatx16 s = qk_tile(it, kDma, true, dp, vprefetch_hook(it - 1, vring));
-    pv_and_softmax(it, s, pprev, vring, kDma, dp);
+    DmaPlan dp_next = dp;
+    const int tn = t_begin + it + 3;
+    pv_and_softmax(it, s, pprev, vring, kDma, dp, [&](int i) {
+      if (i == kPlanStep && tn < t_end) dp_next = dma_plan(tn, (it + 3) % C::NBUF, pages_of(tn));
+    });
+    dp = dp_next;
   }
   const DmaPlan none{nullptr, nullptr, 0u, 0, 0, nullptr, 0u};
   for (; it < ntiles; ++it) {
@@ -752,7 +760,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     __syncthreads();
     bf16x8 vring[PV_PF];
     floatx16 s = qk_tile(it, kNoDma, false, none, vprefetch_hook(it - 1, vring));
-    pv_and_softmax(it, s, pprev, vring, kNoDma, none);
+    pv_and_softmax(it, s, pprev, vring, kNoDma, none, [](int) {});
   }
   // Output update of the last tile.
   {

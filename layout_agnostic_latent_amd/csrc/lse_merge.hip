@@ -11,7 +11,7 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMergeThreads = 128;
-constexpr int kBatch = 8;  // partial rows loaded before they are combined
+constexpr int kBatch = 16;  // partial rows loaded before they are combined
 
 // Parts of a row: either n_parts uniform parts at p * rows + row (the
 // public merge and grid-mode split-KV), or the parts the decode kernel
@@ -50,10 +50,47 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
   const int64_t row = blockIdx.x;
   const auto rp = parts.at(row);
   const int n_parts = rp.n;
-  float M = -INFINITY;
-  for (int p = 0; p < n_parts; ++p) M = fmaxf(M, L[rp.index(p)]);
   const int c4n = d_v >> 2;
   floatx4* orow = (floatx4*)(out + row * d_v);
+  if (n_parts <= kBatch) {
+    // all LSEs in one round of loads, then all partial rows in one more
+    int64_t pi[kBatch];
+    float lp[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      pi[u] = u < n_parts ? rp.index(u) : 0;
+      lp[u] = u < n_parts ? L[pi[u]] : -INFINITY;
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) M = fmaxf(M, lp[u]);
+    if (M == -INFINITY) {  // no live part (NaN LSEs also end here: fmaxf ignores them)
+      for (int c = threadIdx.x; c < c4n; c += kMergeThreads) orow[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (lse_out && threadIdx.x == 0) lse_out[row] = -INFINITY;
+      return;
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) s += u < n_parts ? __expf(lp[u] - M) : 0.0f;
+    const float lse = M + __logf(s);
+    float w[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) w[u] = lp[u] != -INFINITY ? __expf(lp[u] - lse) : 0.0f;
+    for (int c = threadIdx.x; c < c4n; c += kMergeThreads) {
+      floatx4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        v[u] = w[u] != 0.0f ? ((const floatx4*)(P + pi[u] * d_v))[c] : floatx4{0.f, 0.f, 0.f, 0.f};
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) acc += w[u] * v[u];
+      orow[c] = acc;
+    }
+    if (lse_out && threadIdx.x == 0) lse_out[row] = lse;
+    return;
+  }
+  float M = -INFINITY;
+  for (int p = 0; p < n_parts; ++p) M = fmaxf(M, L[rp.index(p)]);
   if (M == -INFINITY) {  // no live part (NaN LSEs also end here: fmaxf ignores them)
     for (int c = threadIdx.x; c < c4n; c += kMergeThreads) orow[c] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (lse_out && threadIdx.x == 0) lse_out[row] = -INFINITY;
