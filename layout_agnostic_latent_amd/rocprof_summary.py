@@ -81,6 +81,8 @@ def main():
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--calib-kernel", default="kv_repack_kernel")
+    ap.add_argument("--calib-fetch", help="FETCH_SIZE run holding the calibration kernel (default: --fetch)")
+    ap.add_argument("--calib-write", help="WRITE_SIZE run holding the calibration kernel (default: --write)")
     ap.add_argument("--calib-read-bytes", type=float)
     ap.add_argument("--calib-write-bytes", type=float)
     ap.add_argument("--bench-json", help="the bench.py JSON line of the traced run (for context)")
@@ -94,11 +96,13 @@ def main():
     if args.fetch and args.write:
         fetch = read_pmc(args.fetch, "FETCH_SIZE")
         write = read_pmc(args.write, "WRITE_SIZE")
+        cfetch = read_pmc(args.calib_fetch or args.fetch, "FETCH_SIZE")
+        cwrite = read_pmc(args.calib_write or args.write, "WRITE_SIZE")
         ck = args.calib_kernel
-        f_scale = args.calib_read_bytes / 1024.0 / statistics.mean(fetch[ck])
-        w_scale = args.calib_write_bytes / 1024.0 / statistics.mean(write[ck])
+        f_scale = args.calib_read_bytes / 1024.0 / statistics.mean(cfetch[ck])
+        w_scale = args.calib_write_bytes / 1024.0 / statistics.mean(cwrite[ck])
         rec["calibration"] = {"kernel": ck, "read_bytes": args.calib_read_bytes, "write_bytes": args.calib_write_bytes,
-                              "fetch_kib_raw": statistics.mean(fetch[ck]), "write_kib_raw": statistics.mean(write[ck]),
+                              "fetch_kib_raw": statistics.mean(cfetch[ck]), "write_kib_raw": statistics.mean(cwrite[ck]),
                               "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
         for k in rec["kernels"]:
             if k in fetch and k in write:
