@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-repack", action="store_true", help="time decode attention alone")
+    ap.add_argument("--handoff", type=int, default=0, metavar="K",
+                    help="instead of the throughput line: spread the repack of a seeded half of the requests over "
+                         "K decode steps on a second stream and report the decode-step slowdown")
     return ap.parse_args()
 
 
@@ -88,6 +91,8 @@ def main():
 
     dev = torch.device("cuda:0")
     case, desc, do_repack, merge_case, splits = build_workload(args.workload)
+    if args.handoff > 0:
+        return run_handoff(args, case, desc, splits)
     if args.no_repack:
         do_repack = False
     B, Hs = case.num_reqs, case.num_q_heads
@@ -214,6 +219,102 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def run_handoff(args, case, desc, splits):
+    """Background handoff on one GPU: the pages of a seeded half of the
+    requests move to a fresh pool in K slices (one per decode step) on a
+    second stream of default priority, while decode attention over the batch
+    runs on the first; both read the same KV pool.  Reports how much longer a
+    decode step takes while the handoff runs (the pages' switch cost: a
+    median below 0.51% of the step, weekinpapers page, Abstract)."""
+    import numpy as np
+    import torch
+
+    import layout_agnostic_latent_amd as sp
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    K = args.handoff
+    B, Hs = case.num_reqs, case.num_q_heads
+    q = torch.from_numpy(case.q.view(np.int16)).to(dev)
+    kv = torch.from_numpy(case.kv_pages.view(np.int16)).to(dev)
+    bt = torch.from_numpy(case.block_table).to(dev)
+    sl = torch.from_numpy(case.seq_lens).to(dev)
+    out = torch.empty((B, Hs, case.d_v), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hs), dtype=torch.float32, device=dev)
+    rc = W.make_repack_case(case, seed=case.seed + 100)
+    dst = torch.zeros((rc.dst_num_pages,) + case.kv_pages.shape[1:], dtype=torch.int16, device=dev)
+    rows = np.array_split(np.arange(rc.src_table.shape[0]), K)
+    slices = [(torch.from_numpy(np.ascontiguousarray(rc.src_table[r])).to(dev),
+               torch.from_numpy(np.ascontiguousarray(rc.dst_table[r])).to(dev)) for r in rows if len(r)]
+    errs = torch.zeros((1,), dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream(device=dev)  # default priority
+    main = torch.cuda.current_stream(dev)
+
+    def decode():
+        sp.decode_attn(q, kv, bt, sl, case.head_lo, case.head_hi, case.tok_lo, case.tok_hi, out, lse,
+                       d_v=case.d_v, scale=case.scale, num_splits=splits, stream=main)
+
+    def repack(i):
+        st, dt = slices[i % len(slices)]
+        sp.kv_repack(kv, st, dst, dt, errs, stream=side)
+
+    def timed(fn, n, streams):
+        starts = {s_: torch.cuda.Event(enable_timing=True) for s_ in streams}
+        ends = {s_: torch.cuda.Event(enable_timing=True) for s_ in streams}
+        torch.cuda.synchronize()
+        for s_ in streams:
+            starts[s_].record(s_)
+        for i in range(n):
+            fn(i)
+        for s_ in streams:
+            ends[s_].record(s_)
+        torch.cuda.synchronize()
+        t0 = min(starts.values(), key=lambda e: 0)  # all recorded back to back
+        return {s_: t0.elapsed_time(ends[s_]) for s_ in streams}
+
+    for _ in range(args.warmup):
+        decode()
+        repack(0)
+    torch.cuda.synchronize()
+    # K decode steps alone, then K steps with one handoff slice each, in
+    # rounds; medians over the rounds
+    n = len(slices)
+    rounds = max(3, min(9, args.steps // max(1, n)))
+    a_s, b_s, r_s, d_s = [], [], [], []
+    for _ in range(rounds):
+        a_s.append(timed(lambda i: decode(), n, [main])[main] / n)
+        both = timed(lambda i: (decode(), repack(i)), n, [main, side])
+        b_s.append(both[main] / n)
+        d_s.append(both[side])
+        r_s.append(timed(lambda i: repack(i), n, [side])[side])
+    alone, step_both = float(np.median(a_s)), float(np.median(b_s))
+    rep_alone, done_after = float(np.median(r_s)), float(np.median(d_s))
+    assert int(errs.item()) == 0 and sp.device_errors(clear=True) == 0
+    moved = rc.dst_num_pages * case.kv_pages[0].nbytes
+    # the handoff really happened: every moved page equals its source
+    src_idx = torch.from_numpy(rc.src_table[rc.src_table >= 0]).long().to(dev)
+    dst_idx = torch.from_numpy(rc.dst_table[rc.dst_table >= 0]).long().to(dev)
+    assert torch.equal(dst[dst_idx], kv[src_idx]), "handoff copy differs from its source"
+    line = {
+        "metric": "decode-step slowdown while a background KV handoff runs on a second stream, 1 GPU",
+        "value": round(100.0 * (step_both / alone - 1.0), 3),
+        "unit": "% of the decode step",
+        "higher_is_better": False,
+        "n_gpus": 1,
+        "steps": n * rounds,
+        "warmup": args.warmup,
+        "data": "synthetic",
+        "config": {"workload": desc, "handoff_slices": n, "moved_pages": int(rc.dst_num_pages),
+                   "moved_bytes": int(moved),
+                   "streams": "decode on the current stream, repack on a second stream, both default priority"},
+        "parts": {"decode_step_alone_us": round(alone * 1e3, 2), "decode_step_during_handoff_us": round(step_both * 1e3, 2),
+                  "repack_alone_us": round(rep_alone * 1e3, 2),
+                  "repack_alone_TBps_rw": round(2 * moved / (rep_alone * 1e-3) / 1e12, 3),
+                  "handoff_done_after_us": round(done_after * 1e3, 2), "rounds": rounds},
+    }
+    print(json.dumps(line))
 
 
 def measured_traffic(workload, kernel_prefix):

@@ -258,6 +258,37 @@ def test_transition_repack_bit_exact(transition):
     assert torch.equal(back[torch.from_numpy(moved).long().to(DEV)], t["kv"][torch.from_numpy(moved).long().to(DEV)])
 
 
+def test_background_handoff_concurrent(transition):
+    """Decode on one stream while the repack runs in slices on a second
+    stream (both default priority), reading the same KV pool: the decode
+    output still matches the oracle and every moved page is exact."""
+    c, t = transition
+    _print("case transition handoff on two streams")
+    rc = W.make_repack_case(c, seed=6)
+    dst = torch.zeros((rc.dst_num_pages,) + c.kv_pages.shape[1:], dtype=torch.int16, device=DEV)
+    errs = torch.zeros((1,), dtype=torch.int32, device=DEV)
+    side = torch.cuda.Stream(device=DEV)
+    main = torch.cuda.current_stream(DEV)
+    out = torch.full((c.num_reqs, c.num_q_heads, c.d_v), float("nan"), dtype=torch.float32, device=DEV)
+    lse = torch.full((c.num_reqs, c.num_q_heads), float("nan"), dtype=torch.float32, device=DEV)
+    rows = np.array_split(np.arange(rc.src_table.shape[0]), 4)
+    for r in rows:
+        sp.decode_attn(t["q"], t["kv"], t["bt"], t["sl"], 0, c.num_q_heads, 0, 1 << 30, out, lse,
+                       d_v=c.d_v, scale=c.scale, stream=main)
+        sp.kv_repack(t["kv"], torch.from_numpy(np.ascontiguousarray(rc.src_table[r])).to(DEV), dst,
+                     torch.from_numpy(np.ascontiguousarray(rc.dst_table[r])).to(DEV), errs, stream=side)
+    torch.cuda.synchronize()
+    assert int(errs.item()) == 0
+    got = dst.cpu().numpy().view(np.uint16)
+    want, copied, rejected = oracle.kv_repack(c.kv_pages, rc.src_table,
+                                              np.zeros((rc.dst_num_pages,) + c.kv_pages.shape[1:], np.uint16),
+                                              rc.dst_table)
+    assert rejected == 0 and np.array_equal(got, want), "repack on the side stream not bit-exact"
+    pick = sorted({int(np.argmin(c.seq_lens)), int(np.argmax(c.seq_lens)), 5, 40})
+    ro, rl = run_oracle(c, reqs=pick)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, rows=pick, what="decode during handoff")
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
