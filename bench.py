@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-repack", action="store_true", help="time decode attention alone")
+    ap.add_argument("--layout-model", action="store_true",
+                    help="instead of the throughput line: time the busiest rank's attention share of each layout "
+                         "(B=16, T=8, H=128, contexts 1k..64k) and pick the cheapest layout per context")
     ap.add_argument("--handoff", type=int, default=0, metavar="K",
                     help="instead of the throughput line: spread the repack of a seeded half of the requests over "
                          "K decode steps on a second stream and report the decode-step slowdown")
@@ -90,6 +93,8 @@ def main():
     import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.layout_model:
+        return run_layout_model(args)
     case, desc, do_repack, merge_case, splits = build_workload(args.workload)
     if args.handoff > 0:
         return run_handoff(args, case, desc, splits)
@@ -313,6 +318,90 @@ def run_handoff(args, case, desc, splits):
                   "repack_alone_us": round(rep_alone * 1e3, 2),
                   "repack_alone_TBps_rw": round(2 * moved / (rep_alone * 1e-3) / 1e12, 3),
                   "handoff_done_after_us": round(done_after * 1e3, 2), "rounds": rounds},
+    }
+    print(json.dumps(line))
+
+
+def run_layout_model(args, B=16, T=8, H=128, contexts=(1024, 4096, 16384, 32768, 65536)):
+    """Attention time per decode step of each layout, as the busiest rank's
+    share time measured at its real shape (layout_model's decomposition of
+    thelatestinai page, Appendix Table 2), and the cheapest layout."""
+    import numpy as np
+    import torch
+
+    import layout_agnostic_latent_amd as sp
+    import workloads as W
+    from layout_agnostic_latent_amd import layout_model as lm
+
+    dev = torch.device("cuda:0")
+
+    def time_share(sh, s):
+        # a rank's share: sh.reqs requests, sh.tokens tokens each (for CP the
+        # range of rank 3 of a history of s tokens), sh.heads query heads
+        if sh.reqs == 0 or sh.tokens == 0:
+            return 0.0
+        cp = sh.merge_parts > 1
+        lo = 3 * s // T if cp else 0
+        hi = lo + sh.tokens if cp else s
+        case = W.make_decode_case("share", 7, [s] * sh.reqs, num_heads=H, d_qk=W.LATENT_QK, d_v=W.LATENT_V,
+                                  page_size=64, scale=W.LATENT_SCALE, head_lo=0, head_hi=sh.heads,
+                                  tok_lo=lo, tok_hi=hi, live_only_in_range=cp)
+        copies = max(2, min(16, math.ceil(6e8 / case.kv_pages.nbytes)))
+        qs = [torch.from_numpy(case.q.view(np.int16)).to(dev) for _ in range(copies)]
+        kvs = [torch.from_numpy(case.kv_pages.view(np.int16)).to(dev) for _ in range(copies)]
+        bt = torch.from_numpy(case.block_table).to(dev)
+        sl = torch.from_numpy(case.seq_lens).to(dev)
+        out = torch.empty((sh.reqs, sh.heads, case.d_v), dtype=torch.float32, device=dev)
+        lse = torch.empty((sh.reqs, sh.heads), dtype=torch.float32, device=dev)
+        # CP: after a reduce-scatter by head, each rank merges T parts of its H/T heads
+        mh = max(1, H // T)
+        parts = torch.randn((T, sh.reqs * mh, case.d_v), dtype=torch.float32, device=dev)
+        plse = torch.rand((T, sh.reqs * mh), dtype=torch.float32, device=dev) * 10 - 5
+        mout = torch.empty((sh.reqs * mh, case.d_v), dtype=torch.float32, device=dev)
+        mlse = torch.empty((sh.reqs * mh,), dtype=torch.float32, device=dev)
+
+        def call(i):
+            k = i % copies
+            sp.decode_attn(qs[k], kvs[k], bt, sl, 0, sh.heads, lo, hi, out, lse, d_v=case.d_v, scale=case.scale)
+            if cp:
+                sp.lse_merge(parts, plse, mout, mlse)
+
+        for i in range(3):
+            call(i)
+        n = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        del qs, kvs
+        torch.cuda.empty_cache()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    rows = []
+    for s in contexts:
+        cache = {}
+
+        def time_of(sh, s=s, cache=cache):
+            if sh not in cache:
+                cache[sh] = time_share(sh, s)
+            return cache[sh]
+
+        best, times = lm.choose(B, T, s, H, time_of)
+        rows.append({"context": s, "attention_us": {k: round(v, 2) for k, v in times.items()}, "best": best})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    line = {
+        "metric": "attention time per decode step of each layout (busiest rank's measured share), 1 GPU",
+        "unit": "us",
+        "higher_is_better": False,
+        "n_gpus": 1,
+        "data": "synthetic",
+        "config": {"workload": f"B={B} requests, T={T} ranks, H={H} query heads, one 576-dim latent KV head, page 64",
+                   "shares": "TP: H/T heads of every request; CP: 1/T of every request's tokens + merge of T parts "
+                             "over H/T heads; DP-attention/DOP: ceil(B/T) whole requests"},
+        "rows": rows,
     }
     print(json.dumps(line))
 

@@ -10,8 +10,9 @@ namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMergeThreads = 128;
-constexpr int kBatch = 16;  // partial rows loaded before they are combined
+constexpr int kMergeThreads = 256;
+constexpr int kLdsParts = 2048;  // parts whose weights are kept in LDS (more are recomputed)
+constexpr int kBatch = 8;        // partial rows a thread loads before combining them
 
 // Parts of a row: either n_parts uniform parts at p * rows + row (the
 // public merge and grid-mode split-KV), or the parts the decode kernel
@@ -40,89 +41,97 @@ struct ListedParts {
   }
 };
 
-// One workgroup per row; each thread owns float4 columns.  The row's LSEs
-// (a few floats) are read by every thread from L1/L2.
+// Block-wide reductions over kMergeThreads threads through LDS.
+__device__ float block_max(float v, float* red) {
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < kMergeThreads / 64; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+__device__ float block_sum(float v, float* red) {
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = 0.0f;
+  for (int w = 0; w < kMergeThreads / 64; ++w) r += red[w];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup per output row.  The row's LSEs are loaded by all threads at
+// once (one round of loads) and reduced through LDS; the weights
+// exp(L_p - L) stay in LDS.  The partial rows are then read by G groups of
+// threads (G = threads / float4 columns), each group taking every G-th
+// part, kBatch loads in flight per thread; the groups' sums meet in LDS.
 template <typename Parts>
 __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* __restrict__ P,
                                                                   const float* __restrict__ L, Parts parts,
                                                                   int32_t d_v, float* __restrict__ out,
                                                                   float* __restrict__ lse_out) {
+  __shared__ float w_s[kLdsParts];
+  __shared__ floatx4 acc_s[kMergeThreads];
+  __shared__ float red[kMergeThreads / 64];
+  const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const auto rp = parts.at(row);
-  const int n_parts = rp.n;
+  const int n = rp.n;
   const int c4n = d_v >> 2;
   floatx4* orow = (floatx4*)(out + row * d_v);
-  if (n_parts <= kBatch) {
-    // all LSEs in one round of loads, then all partial rows in one more
-    int64_t pi[kBatch];
-    float lp[kBatch];
+
+  float m = -INFINITY;
+  for (int p = tid; p < n; p += kMergeThreads) {
+    const float l = L[rp.index(p)];
+    if (p < kLdsParts) w_s[p] = l;
+    m = fmaxf(m, l);
+  }
+  const float M = block_max(m, red);
+  if (M == -INFINITY) {  // no live part (NaN LSEs also end here: fmaxf ignores them)
+    for (int c = tid; c < c4n; c += kMergeThreads) orow[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (lse_out && tid == 0) lse_out[row] = -INFINITY;
+    return;
+  }
+  float sum = 0.0f;
+  for (int p = tid; p < n; p += kMergeThreads) sum += __expf((p < kLdsParts ? w_s[p] : L[rp.index(p)]) - M);
+  const float lse = M + __logf(block_sum(sum, red));
+  for (int p = tid; p < n && p < kLdsParts; p += kMergeThreads) w_s[p] = __expf(w_s[p] - lse);  // -inf -> 0
+  __syncthreads();
+
+  const int G = c4n < kMergeThreads ? kMergeThreads / c4n : 1;  // part groups
+  const int g = tid / (c4n < kMergeThreads ? c4n : kMergeThreads);
+  for (int c0 = 0; c0 < c4n; c0 += kMergeThreads / G) {
+    const int c = c0 + tid % (kMergeThreads / G);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (g < G && c < c4n) {
+      for (int p0 = g * kBatch; p0 < n; p0 += G * kBatch) {
+        floatx4 v[kBatch];
+        float w[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      pi[u] = u < n_parts ? rp.index(u) : 0;
-      lp[u] = u < n_parts ? L[pi[u]] : -INFINITY;
+        for (int u = 0; u < kBatch; ++u) {
+          const int p = p0 + u;
+          const int64_t pi = p < n ? rp.index(p) : 0;
+          w[u] = p >= n ? 0.0f : (p < kLdsParts ? w_s[p] : __expf(L[pi] - lse));
+          v[u] = w[u] != 0.0f ? ((const floatx4*)(P + pi * d_v))[c] : floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) acc += w[u] * v[u];
+      }
     }
-    float M = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) M = fmaxf(M, lp[u]);
-    if (M == -INFINITY) {  // no live part (NaN LSEs also end here: fmaxf ignores them)
-      for (int c = threadIdx.x; c < c4n; c += kMergeThreads) orow[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (lse_out && threadIdx.x == 0) lse_out[row] = -INFINITY;
-      return;
-    }
-    float s = 0.0f;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) s += u < n_parts ? __expf(lp[u] - M) : 0.0f;
-    const float lse = M + __logf(s);
-    float w[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) w[u] = lp[u] != -INFINITY ? __expf(lp[u] - lse) : 0.0f;
-    for (int c = threadIdx.x; c < c4n; c += kMergeThreads) {
-      floatx4 v[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        v[u] = w[u] != 0.0f ? ((const floatx4*)(P + pi[u] * d_v))[c] : floatx4{0.f, 0.f, 0.f, 0.f};
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) acc += w[u] * v[u];
+    if (G > 1) {
+      acc_s[tid] = acc;
+      __syncthreads();
+      if (g == 0 && c < c4n) {
+        for (int j = 1; j < G; ++j) acc += acc_s[tid + j * c4n];
+        orow[c] = acc;
+      }
+      __syncthreads();
+    } else if (c < c4n) {
       orow[c] = acc;
     }
-    if (lse_out && threadIdx.x == 0) lse_out[row] = lse;
-    return;
   }
-  float M = -INFINITY;
-  for (int p = 0; p < n_parts; ++p) M = fmaxf(M, L[rp.index(p)]);
-  if (M == -INFINITY) {  // no live part (NaN LSEs also end here: fmaxf ignores them)
-    for (int c = threadIdx.x; c < c4n; c += kMergeThreads) orow[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (lse_out && threadIdx.x == 0) lse_out[row] = -INFINITY;
-    return;
-  }
-  float s = 0.0f;
-  for (int p = 0; p < n_parts; ++p) s += __expf(L[rp.index(p)] - M);
-  const float lse = M + __logf(s);
-  for (int c = threadIdx.x; c < c4n; c += kMergeThreads) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    // kBatch parts' loads in flight at once; empty parts load nothing
-    for (int p0 = 0; p0 < n_parts; p0 += kBatch) {
-      floatx4 v[kBatch];
-      float w[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int p = p0 + u;
-        const int64_t pi = p < n_parts ? rp.index(p) : 0;
-        const float lp = p < n_parts ? L[pi] : -INFINITY;
-        w[u] = 0.0f;
-        v[u] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (lp != -INFINITY) {
-          w[u] = __expf(lp - lse);
-          v[u] = ((const floatx4*)(P + pi * d_v))[c];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) acc += w[u] * v[u];
-    }
-    orow[c] = acc;
-  }
-  if (lse_out && threadIdx.x == 0) lse_out[row] = lse;
+  if (lse_out && tid == 0) lse_out[row] = lse;
 }
 
 }  // namespace

@@ -397,6 +397,22 @@ def test_merge_edges():
     assert torch.allclose(o1[live], P[0][live], atol=1e-6, rtol=0)
 
 
+@pytest.mark.parametrize("n_parts,rows,d_v", [(300, 7, 512), (3000, 3, 64), (17, 33, 512), (1, 4, 64)])
+def test_merge_many_parts(n_parts, rows, d_v):
+    """Part counts past the LDS weight store (2,048) and narrow rows (many part
+    groups per row); some parts empty."""
+    g = torch.Generator(device="cpu").manual_seed(n_parts)
+    P = torch.randn((n_parts, rows, d_v), generator=g, dtype=torch.float32).to(DEV)
+    L = (torch.rand((n_parts, rows), generator=g, dtype=torch.float32) * 20 - 10).to(DEV)
+    L[::7, 0] = -math.inf
+    out = torch.empty((rows, d_v), dtype=torch.float32, device=DEV)
+    lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    sp.lse_merge(P, L, out, lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.lse_merge(P.cpu().numpy(), L.cpu().numpy())
+    assert_close(out.cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl, what=f"merge {n_parts} parts")
+
+
 def test_repack_rejects_bad_pairs():
     src = torch.arange(6 * 4 * 8, dtype=torch.int16, device=DEV).view(6, 4, 8)
     dst = torch.full((5, 4, 8), -1, dtype=torch.int16, device=DEV)
