@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="owner",
-                    help="owner | tp | cp | transition | sweep:<owner|tp|cp>:<ctx>")
+                    help="owner | tp | cp | transition | sweep:<owner|tp|cp|gqa<G>>:<ctx>")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -167,7 +167,8 @@ def main():
     repack_us = 1e3 * prof["repack_ms"] / max(1, prof["repack_launches"])
 
     # algorithmic bytes and flops of one decode-attention call
-    dec_bytes = (kv_tokens * KV_ROW_BYTES + B * Hs * case.d_qk * 2 + B * Hs * case.d_v * 4 + B * Hs * 4
+    dec_bytes = (kv_tokens * KV_ROW_BYTES * case.num_kv_heads + B * Hs * case.d_qk * 2 + B * Hs * case.d_v * 4
+                 + B * Hs * 4
                  + case.block_table.nbytes + case.seq_lens.nbytes)
     dec_flops = 2.0 * Hs * (case.d_qk + case.d_v) * kv_tokens
     achieved = dec_bytes / (dec_us * 1e-6) / 1e9

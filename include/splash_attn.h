@@ -65,20 +65,25 @@ typedef struct splash_desc {
   int32_t num_pages;         /* pages in the pool (valid physical page ids are [0, num_pages)) */
   int32_t num_splits;        /* split-KV chunks per request; 0 = library's choice (env SPLASH_NUM_SPLITS overrides) */
   float scale;               /* softmax scale applied to q.k, e.g. 1/sqrt(192) */
+  int32_t num_kv_heads;      /* G latent KV heads per token (0 or 1: one); num_heads must be a multiple */
 } splash_desc;
 
 /*
  * Decode attention of one share.  For each request b < num_reqs and each head
  * h in [head_lo, head_hi):
+ *   g = h / (num_heads / G)   (query heads share KV heads in contiguous groups)
  *   lo = max(tok_lo, 0), hi = min(tok_hi, seq_lens[b])
- *   k_t = kv_pages[block_table[b][t / page_size]][t % page_size][0 .. d_qk)
+ *   k_t = kv_pages[block_table[b][t / page_size]][t % page_size][g][0 .. d_qk)
  *   v_t = k_t[0 .. d_v)
  *   out[b][h - head_lo][:] = sum_t softmax_t(scale * q[b][h] . k_t) v_t   over t in [lo, hi)
  *   lse[b][h - head_lo]    = log(sum_t exp(scale * q[b][h] . k_t))       (natural log)
  * An empty range gives out = 0 and lse = -inf.
  *
  *   q            bf16 [num_reqs][num_heads][d_qk], rows contiguous
- *   kv_pages     bf16 [num_pages][page_size][d_qk]
+ *   kv_pages     bf16 [num_pages][page_size][G][d_qk] (G = num_kv_heads; the
+ *                premise is attention with few or no KV heads, weekinpapers
+ *                page, Abstract: G = 1 is the latent-KV case, G > 1 groups
+ *                the query heads onto a few shared KV heads)
  *   block_table  int32 [num_reqs][max_pages_per_req]; only the entries that
  *                cover [lo, hi) are read.  An entry outside [0, num_pages) is
  *                read as page 0 and raises SPLASH_DEVERR_BAD_PAGE.
@@ -88,10 +93,13 @@ typedef struct splash_desc {
  * The work is split into KV chunks (split-KV) when the share is too small to
  * fill the GPU; partials then go to a library-owned workspace (allocated on
  * first need, grown on demand, freed by splash_release_workspace) and are
- * merged on the same stream.  Growing the workspace synchronises the device,
+ * merged on the same stream.  With G > 1 the heads of each KV head the share
+ * touches are one such launch (and merge), in order on the stream.
+ * Growing the workspace synchronises the device,
  * so a call that needs more workspace must not be made under stream capture.
  * Errors: SPLASH_EINVAL for null pointers, non-positive sizes, head range
- * outside [0, num_heads) or empty, tok_hi < tok_lo; SPLASH_EUNSUPPORTED for
+ * outside [0, num_heads) or empty, tok_hi < tok_lo, num_kv_heads < 0 or not
+ * dividing num_heads; SPLASH_EUNSUPPORTED for
  * (d_qk, d_v) not in {(576, 512), (80, 64)} or an unsupported page_size.
  */
 int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pages,

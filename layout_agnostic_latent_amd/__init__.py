@@ -37,7 +37,8 @@ class SplashError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [("num_reqs", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("d_qk", ctypes.c_int32),
                 ("d_v", ctypes.c_int32), ("page_size", ctypes.c_int32), ("max_pages_per_req", ctypes.c_int32),
-                ("num_pages", ctypes.c_int32), ("num_splits", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("num_pages", ctypes.c_int32), ("num_splits", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("num_kv_heads", ctypes.c_int32)]
 
 
 class Profile(ctypes.Structure):
@@ -97,16 +98,20 @@ def _stream(stream) -> int:
 
 
 def make_desc(num_reqs, num_heads, d_qk, d_v, page_size, max_pages_per_req, num_pages, scale,
-              num_splits=0) -> Desc:
-    return Desc(num_reqs, num_heads, d_qk, d_v, page_size, max_pages_per_req, num_pages, num_splits, scale)
+              num_splits=0, num_kv_heads=1) -> Desc:
+    return Desc(num_reqs, num_heads, d_qk, d_v, page_size, max_pages_per_req, num_pages, num_splits, scale,
+                num_kv_heads)
 
 
 def _desc_from(q, kv_pages, block_table, d_v, scale, num_splits) -> Desc:
     B, H, d_qk = q.shape
-    num_pages, ps, d_row = kv_pages.shape
+    if kv_pages.dim() == 3:   # one latent KV head
+        (num_pages, ps, d_row), G = kv_pages.shape, 1
+    else:                     # [P, ps, G, d_qk]: G shared KV heads
+        num_pages, ps, G, d_row = kv_pages.shape
     if d_row != d_qk:
         raise ValueError(f"kv row width {d_row} != q width {d_qk}")
-    return make_desc(B, H, d_qk, d_v, ps, block_table.shape[1], num_pages, scale, num_splits)
+    return make_desc(B, H, d_qk, d_v, ps, block_table.shape[1], num_pages, scale, num_splits, G)
 
 
 def _require(t, name, dtypes, ndim):
@@ -123,12 +128,13 @@ def _require(t, name, dtypes, ndim):
 
 def decode_attn(q, kv_pages, block_table, seq_lens, head_lo: int, head_hi: int, tok_lo: int, tok_hi: int,
                 out, lse=None, *, d_v: int, scale: float, num_splits: int = 0, stream=None) -> None:
-    """splash_decode_attn.  q bf16 [B,H,d_qk]; kv_pages bf16 [P,ps,d_qk]; block_table int32 [B,max_pages];
-    seq_lens int32 [B]; out fp32 [B, head_hi-head_lo, d_v]; lse fp32 [B, head_hi-head_lo] or None."""
+    """splash_decode_attn.  q bf16 [B,H,d_qk]; kv_pages bf16 [P,ps,d_qk] or [P,ps,G,d_qk] (G shared KV heads);
+    block_table int32 [B,max_pages]; seq_lens int32 [B]; out fp32 [B, head_hi-head_lo, d_v];
+    lse fp32 [B, head_hi-head_lo] or None."""
     import torch
     bf = (torch.bfloat16, torch.int16, torch.uint16)
     _require(q, "q", bf, 3)
-    _require(kv_pages, "kv_pages", bf, 3)
+    _require(kv_pages, "kv_pages", bf, 4 if getattr(kv_pages, "ndim", 3) == 4 else 3)
     _require(block_table, "block_table", (torch.int32,), 2)
     _require(seq_lens, "seq_lens", (torch.int32,), 1)
     _require(out, "out", (torch.float32,), 3)
@@ -146,9 +152,10 @@ def decode_attn(q, kv_pages, block_table, seq_lens, head_lo: int, head_hi: int, 
 
 
 def decode_plan(num_reqs, num_heads, d_qk, d_v, page_size, max_pages_per_req, num_pages, scale,
-                head_lo, head_hi, tok_lo, tok_hi, num_splits=0) -> Tuple[int, int, int]:
+                head_lo, head_hi, tok_lo, tok_hi, num_splits=0, num_kv_heads=1) -> Tuple[int, int, int]:
     """(split-KV chunks, head groups, workspace bytes) the library would use.  Host only."""
-    d = make_desc(num_reqs, num_heads, d_qk, d_v, page_size, max_pages_per_req, num_pages, scale, num_splits)
+    d = make_desc(num_reqs, num_heads, d_qk, d_v, page_size, max_pages_per_req, num_pages, scale, num_splits,
+                  num_kv_heads)
     s, g, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
     _check(lib().splash_decode_plan(ctypes.byref(d), head_lo, head_hi, tok_lo, tok_hi, ctypes.byref(s),
                                     ctypes.byref(g), ctypes.byref(w)))

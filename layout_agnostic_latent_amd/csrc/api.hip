@@ -160,8 +160,14 @@ WorklistLayout worklist_layout(int64_t items, int64_t B, int64_t hs, int64_t d_v
   return w;
 }
 
+// Latent KV heads of the pool (0 in the descriptor means one).
+int kv_heads_of(const splash_desc* d) { return d->num_kv_heads > 0 ? d->num_kv_heads : 1; }
+
 int validate_decode(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t tok_lo, int32_t tok_hi) {
   if (!d) return fail(SPLASH_EINVAL, "desc is NULL");
+  if (d->num_kv_heads < 0) return fail(SPLASH_EINVAL, "num_kv_heads = %d < 0", d->num_kv_heads);
+  if (d->num_heads > 0 && d->num_heads % kv_heads_of(d))
+    return fail(SPLASH_EINVAL, "num_heads = %d not a multiple of num_kv_heads = %d", d->num_heads, d->num_kv_heads);
   if (d->num_reqs < 0) return fail(SPLASH_EINVAL, "num_reqs = %d < 0", d->num_reqs);
   if (d->num_heads <= 0) return fail(SPLASH_EINVAL, "num_heads = %d <= 0", d->num_heads);
   if (d->max_pages_per_req <= 0) return fail(SPLASH_EINVAL, "max_pages_per_req = %d <= 0", d->max_pages_per_req);
@@ -277,39 +283,53 @@ int splash_decode_plan(const splash_desc* desc, int32_t head_lo, int32_t head_hi
   Plan p;
   int rc = make_plan(desc, head_lo, head_hi, tok_lo, tok_hi, &p);
   if (rc) return rc;
+  // per KV head: the first one's split and head-group counts; the largest
+  // workspace (the launches run in order and share it)
+  const int group = desc->num_heads / kv_heads_of(desc);
+  int64_t ws = 0;
+  bool first = true;
+  for (int g = head_lo / group; g * group < head_hi; ++g) {
+    const int lo = head_lo > g * group ? head_lo : g * group;
+    const int hi = head_hi < (g + 1) * group ? head_hi : (g + 1) * group;
+    Plan pg;
+    if ((rc = make_plan(desc, lo, hi, tok_lo, tok_hi, &pg))) return rc;
+    if (first) p = pg;
+    first = false;
+    if (pg.workspace_bytes > ws) ws = pg.workspace_bytes;
+  }
   if (num_splits) *num_splits = p.grid_splits;
   if (head_groups) *head_groups = p.head_groups;
-  if (workspace_bytes) *workspace_bytes = p.workspace_bytes;
+  if (workspace_bytes) *workspace_bytes = ws;
   return SPLASH_OK;
 }
 
-int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pages, const int32_t* block_table,
-                       const int32_t* seq_lens, int32_t head_lo, int32_t head_hi, int32_t tok_lo, int32_t tok_hi,
-                       float* out, float* lse, hipStream_t stream) {
+}  // extern "C"
+
+namespace splash {
+namespace {
+
+// Decode attention of the heads [head_lo, head_hi) that share one latent KV
+// head: `kv` points at that head's row of token 0 of page 0, `kv_row` is the
+// pool's elements per token (G * d_qk), and the results go to heads
+// [out_head0, out_head0 + hs) of out / lse rows of out_heads heads.
+int decode_one_kv_head(const splash_desc* desc, const void* q, const uint16_t* kv, int32_t kv_row,
+                       const int32_t* block_table, const int32_t* seq_lens, int32_t head_lo, int32_t head_hi,
+                       int32_t tok_lo, int32_t tok_hi, float* out, float* lse, int32_t out_heads,
+                       int32_t out_head0, int dev, int32_t* dev_err, hipStream_t stream) {
   Plan p;
   int rc = make_plan(desc, head_lo, head_hi, tok_lo, tok_hi, &p);
   if (rc) return rc;
-  if (!q || !kv_pages || !block_table || !seq_lens || !out)
-    return fail(SPLASH_EINVAL, "null tensor pointer (q, kv_pages, block_table, seq_lens and out are required)");
-  if ((((uintptr_t)q) & 15) || (((uintptr_t)kv_pages) & 15) || (((uintptr_t)out) & 15))
-    return fail(SPLASH_EINVAL, "q, kv_pages and out must be 16-byte aligned");
-  if (desc->num_reqs == 0) return SPLASH_OK;
   const int hs = head_hi - head_lo;
-
-  int dev;
-  if ((rc = current_device(&dev))) return rc;
-  std::lock_guard<std::mutex> lock(g_mu);
-  int32_t* dev_err;
-  if ((rc = device_error_word(dev, &dev_err))) return rc;
 
   DecodeArgs a{};
   a.q = (const uint16_t*)q;
-  a.kv = (const uint16_t*)kv_pages;
+  a.kv = kv;
   a.bt = block_table;
   a.seq_lens = seq_lens;
   a.dev_err = dev_err;
   a.q_req_stride = (int64_t)desc->num_heads * desc->d_qk;
-  a.page_stride = (int64_t)desc->page_size * desc->d_qk;
+  a.kv_row = kv_row;
+  a.page_stride = (int64_t)desc->page_size * kv_row;
   a.max_pages = desc->max_pages_per_req;
   a.num_pages = desc->num_pages;
   a.page_shift = page_shift_of(desc->page_size);
@@ -327,11 +347,18 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
     a.lse = lse;
     a.out_split_stride = 0;
     a.lse_split_stride = 0;
+    a.out_heads = out_heads;
+    a.out_head0 = out_head0;
     a.partial_out = 0;
     hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
     if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
     return SPLASH_OK;
   }
+  // split-KV: partials in the workspace (rows of this launch's hs heads),
+  // then the merge writes the caller's rows
+  a.out_heads = hs;
+  a.out_head0 = 0;
+  const MergeOut om{hs, out_heads, out_head0};
   void* ws;
   if ((rc = ensure_workspace(dev, (size_t)p.workspace_bytes, &ws))) return rc;
   const int64_t rows = (int64_t)desc->num_reqs * hs;
@@ -356,7 +383,7 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
     if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
     e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
       return launch_lse_merge_segmented(part_o, part_l, req_info, (int32_t)rows, hs, desc->d_v, out, lse, stream, e0,
-                                        e1);
+                                        e1, om);
     });
     if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
     return SPLASH_OK;
@@ -371,9 +398,46 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
   hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
   if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
   e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
-    return launch_lse_merge(part_o, part_l, p.grid_splits, (int32_t)rows, desc->d_v, out, lse, stream, e0, e1);
+    return launch_lse_merge(part_o, part_l, p.grid_splits, (int32_t)rows, desc->d_v, out, lse, stream, e0, e1, om);
   });
   if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
+  return SPLASH_OK;
+}
+
+}  // namespace
+}  // namespace splash
+
+extern "C" {
+
+int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pages, const int32_t* block_table,
+                       const int32_t* seq_lens, int32_t head_lo, int32_t head_hi, int32_t tok_lo, int32_t tok_hi,
+                       float* out, float* lse, hipStream_t stream) {
+  Plan p;
+  int rc = make_plan(desc, head_lo, head_hi, tok_lo, tok_hi, &p);  // validates the descriptor and ranges
+  if (rc) return rc;
+  if (!q || !kv_pages || !block_table || !seq_lens || !out)
+    return fail(SPLASH_EINVAL, "null tensor pointer (q, kv_pages, block_table, seq_lens and out are required)");
+  if ((((uintptr_t)q) & 15) || (((uintptr_t)kv_pages) & 15) || (((uintptr_t)out) & 15))
+    return fail(SPLASH_EINVAL, "q, kv_pages and out must be 16-byte aligned");
+  if (desc->num_reqs == 0) return SPLASH_OK;
+  const int hs = head_hi - head_lo;
+  const int G = kv_heads_of(desc);
+  const int group = desc->num_heads / G;
+
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  int32_t* dev_err;
+  if ((rc = device_error_word(dev, &dev_err))) return rc;
+  // one launch (decode, and merge when split) per KV head the share touches
+  for (int g = head_lo / group; g * group < head_hi; ++g) {
+    const int lo = head_lo > g * group ? head_lo : g * group;
+    const int hi = head_hi < (g + 1) * group ? head_hi : (g + 1) * group;
+    rc = decode_one_kv_head(desc, q, (const uint16_t*)kv_pages + (int64_t)g * desc->d_qk, G * desc->d_qk,
+                            block_table, seq_lens, lo, hi, tok_lo, tok_hi, out, lse, hs, lo - head_lo, dev, dev_err,
+                            stream);
+    if (rc) return rc;
+  }
   return SPLASH_OK;
 }
 

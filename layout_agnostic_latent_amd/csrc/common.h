@@ -18,7 +18,10 @@ struct DecodeArgs {
   float* lse;                // fp32 [splits][B][Hs], may be null when splits = 1
   int32_t* dev_err;          // library device error word
   int64_t q_req_stride;      // H * d_qk
-  int64_t page_stride;       // page_size * d_qk
+  int64_t page_stride;       // page_size * kv_row
+  int32_t kv_row;            // elements per token in the pool: G * d_qk (kv points at this launch's KV head)
+  int32_t out_heads;         // heads per request row of out / lse (their row stride)
+  int32_t out_head0;         // out / lse head of this launch's first head
   int64_t out_split_stride;  // B * Hs * d_v
   int64_t lse_split_stride;  // B * Hs
   int32_t max_pages;
@@ -59,9 +62,17 @@ struct DecodeVariant {
 hipError_t launch_decode(const DecodeVariant& v, dim3 grid, const DecodeArgs& a, hipStream_t stream,
                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
+// Output rows of a merge: row r = (b, h) with b = r / hs, h = r % hs goes to
+// out row b * out_heads + out_head0 + h (the identity when out_heads = hs
+// and out_head0 = 0).
+struct MergeOut {
+  int32_t hs, out_heads, out_head0;
+};
+
 hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows,
                             int32_t d_v, float* out, float* lse_out, hipStream_t stream,
-                            hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                            hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                            MergeOut om = MergeOut{0, 0, 0});
 
 // Work-list mode handles batches of up to this many requests.
 constexpr int kPlanMaxReqs = 8192;
@@ -70,7 +81,8 @@ constexpr int kPlanMaxReqs = 8192;
 // req_info[b] (rows = B * hs).
 hipError_t launch_lse_merge_segmented(const float* partials, const float* lses, const int4* req_info, int32_t rows,
                                       int32_t hs, int32_t d_v, float* out, float* lse_out, hipStream_t stream,
-                                      hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                                      hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                                      MergeOut om = MergeOut{0, 0, 0});
 
 hipError_t launch_kv_repack(const void* src, const int32_t* src_table, void* dst, const int32_t* dst_table,
                             int64_t n_pairs, int64_t page_bytes, int32_t src_num_pages,

@@ -219,7 +219,6 @@ template <int D_QK, int D_V, int WH, int WV>
 struct Cfg {
   static constexpr int NW = WH * WV;
   static constexpr int NTHREADS = 64 * NW;
-  static constexpr int ROWG = D_QK * 2;              // bytes of a KV row in HBM
   static constexpr int NCH = D_QK / 8;               // 16-B chunks per KV row
   static constexpr int NSLAB = (NCH + 7) / 8;        // 128-B slabs per row (8 chunks each)
   static constexpr int SLAB_B = kTileTok * 128;      // LDS bytes of one slab of a tile
@@ -301,8 +300,9 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   const int mlo = max(lo, t_begin * kTileTok);
   const int mhi = min(hi, t_end * kTileTok);
 
-  float* out_row = a.out + split * a.out_split_stride + ((int64_t)b_out * a.n_heads + hs_safe) * D_V;
-  float* lse_ptr = a.lse ? a.lse + split * a.lse_split_stride + (int64_t)b_out * a.n_heads + hs_safe : nullptr;
+  float* out_row = a.out + split * a.out_split_stride + ((int64_t)b_out * a.out_heads + a.out_head0 + hs_safe) * D_V;
+  float* lse_ptr =
+      a.lse ? a.lse + split * a.lse_split_stride + (int64_t)b_out * a.out_heads + a.out_head0 + hs_safe : nullptr;
 
   if (t_end <= t_begin) {  // empty chunk: O = 0, LSE = -inf
     // A split-KV partial with LSE = -inf is never read by the merge, so only
@@ -324,6 +324,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   bf16x8 qf[C::KS];  // Q of this wave's 32 heads (loaded after the first DMAs)
   const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   const int ps_mask = (1 << a.page_shift) - 1;
+  const int row_b = a.kv_row * 2;  // bytes from one token's row to the next in the pool
   const bool one_page_per_tile = a.page_shift >= 5;
   bool bad_page = false;  // reported once, after the last DMA has completed
 
@@ -387,8 +388,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // 16 or more rows and start at multiples of 16), even after clamping, so
   // every DMA takes a wave-uniform base address and a 32-bit per-lane offset.
   struct DmaPlan {
-    const char* base0;  // + row * ROWG: rows on page p0
-    const char* base1;  // + row * ROWG: rows 16..31 on page p1
+    const char* base0;  // + row * row_b: rows on page p0
+    const char* base1;  // + row * row_b: rows 16..31 on page p1
     uint32_t lds;       // ring slot
     int rlo, rhi1;      // valid rows of the tile
     // four waves: wave w's instructions all carry rows 8w .. 8w+7 and differ
@@ -399,15 +400,15 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   auto dma_plan = [&](int t, int slot, TilePages pg) -> DmaPlan {
     const int tok0 = t * kTileTok;
     DmaPlan d;
-    d.base0 = (const char*)(a.kv + (int64_t)pg.p0 * a.page_stride + (int64_t)(tok0 & ps_mask) * D_QK);
-    d.base1 = (const char*)(a.kv + (int64_t)pg.p1 * a.page_stride) - 16 * C::ROWG;
+    d.base0 = (const char*)(a.kv + (int64_t)pg.p0 * a.page_stride + (int64_t)(tok0 & ps_mask) * a.kv_row);
+    d.base1 = (const char*)(a.kv + (int64_t)pg.p1 * a.page_stride) - 16 * row_b;
     d.lds = smem_base + slot * C::TILE_B;
     d.rlo = max(mlo - tok0, 0);
     d.rhi1 = min(mhi - tok0, kTileTok) - 1;
     if constexpr (C::NW == 4 && !C::PADDED) {
       const int R = 8 * wave;
       const int row = min(max(R + l8, d.rlo), d.rhi1);
-      d.voff = (uint32_t)(row * C::ROWG + 16 * ((lane & 7) ^ (int)row_swizzle(R + l8)));
+      d.voff = (uint32_t)(row * row_b + 16 * ((lane & 7) ^ (int)row_swizzle(R + l8)));
       d.wbase = (one_page_per_tile || min(max(R, d.rlo), d.rhi1) < 16) ? d.base0 : d.base1;
     } else {
       d.voff = 0;
@@ -426,7 +427,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     int chunk = 8 * (nn / 4) + ((lane & 7) ^ (int)row_swizzle(R + l8));
     if (C::PADDED && chunk >= C::NCH) chunk = 0;  // slab padding: any in-row chunk
     const char* base = (one_page_per_tile || min(max(R, d.rlo), d.rhi1) < 16) ? d.base0 : d.base1;
-    lds_dma16_s(base, (uint32_t)(row * C::ROWG + chunk * 16), d.lds + nn * 1024);
+    lds_dma16_s(base, (uint32_t)(row * row_b + chunk * 16), d.lds + nn * 1024);
   };
 
   // ---- online-softmax state (per head = per lane column) ----
@@ -785,7 +786,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   {
     float* stage = (float*)smem + wave * 32 * C::PITCH;
     const int head0 = (blockIdx.z * WH + wh) * 32;  // first head of this wave within the share
-    float* out_base = a.out + split * a.out_split_stride + ((int64_t)b_out * a.n_heads + head0) * D_V;
+    float* out_base = a.out + split * a.out_split_stride + ((int64_t)b_out * a.out_heads + a.out_head0 + head0) * D_V;
     constexpr int ROWF = C::PB * 32;  // staged floats per row and pass
 #pragma unroll
     for (int pass = 0; pass < C::VB / C::PB; ++pass) {

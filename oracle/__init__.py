@@ -64,20 +64,29 @@ def decode_attn(q: np.ndarray, kv_pages: np.ndarray, block_table: np.ndarray,
     """Decode attention of one share, by definition, in float64.
 
     q           uint16 bf16 bits [B, H, d_qk]
-    kv_pages    uint16 bf16 bits [num_pages, page_size, d_qk]
+    kv_pages    uint16 bf16 bits [num_pages, page_size, d_qk] (one latent KV
+                head), or [num_pages, page_size, G, d_qk] (G shared KV heads)
     block_table int32 [B, max_pages]: logical page j of request b -> physical page
     seq_lens    int32 [B]
     Returns (out float64 [B, head_hi-head_lo, d_v], lse float64 [B, head_hi-head_lo]).
     Requests not listed in ``reqs`` (default: all) are left as O = 0, LSE = -inf.
 
-    Per request b and head h of the slice:
+    Per request b and head h of the slice (h an index of q's H heads):
+      g = h // (H / G), the KV head that query head h shares with its group
       lo = max(tok_lo, 0), hi = min(tok_hi, seq_len[b]); empty -> O = 0, LSE = -inf
-      k_t = kv[block_table[b][t // page_size], t % page_size, :d_qk], v_t = k_t[:d_v]
+      k_t = kv[block_table[b][t // page_size], t % page_size, (g,) :d_qk], v_t = k_t[:d_v]
       s_t = scale * q[b,h] . k_t
       O   = sum_t exp(s_t - m) v_t / sum_t exp(s_t - m),  m = max_t s_t
       LSE = m + log(sum_t exp(s_t - m))
+    The premise is attention with few or no KV heads (weekinpapers page,
+    Abstract); with G > 1 the query heads are taken to share KV heads in
+    contiguous groups of H / G.
     """
     B, H, d_qk = q.shape
+    G = 1 if kv_pages.ndim == 3 else kv_pages.shape[2]
+    if H % G:
+        raise ValueError("the query heads must split evenly over the KV heads")
+    group = H // G
     Hs = head_hi - head_lo
     out = np.zeros((B, Hs, d_v), dtype=np.float64)
     lse = np.full((B, Hs), -np.inf, dtype=np.float64)
@@ -88,15 +97,20 @@ def decode_attn(q: np.ndarray, kv_pages: np.ndarray, block_table: np.ndarray,
             continue
         t = np.arange(lo, hi)
         pages = block_table[b, t // page_size]
-        K = widen_bf16(kv_pages[pages, t % page_size, :d_qk])   # [n, d_qk]
-        V = K[:, :d_v]                                           # [n, d_v]
-        Q = widen_bf16(q[b, head_lo:head_hi, :])                 # [Hs, d_qk]
-        S = scale * (Q @ K.T)                                    # [Hs, n]
-        m = S.max(axis=1, keepdims=True)
-        W = np.exp(S - m)
-        denom = W.sum(axis=1, keepdims=True)
-        out[b] = (W @ V) / denom
-        lse[b] = (m + np.log(denom))[:, 0]
+        rows = kv_pages[pages, t % page_size]                     # [n, d_qk] or [n, G, d_qk]
+        for g in range(G):
+            h0, h1 = max(head_lo, g * group), min(head_hi, (g + 1) * group)
+            if h0 >= h1:
+                continue
+            K = widen_bf16(rows[:, :d_qk] if G == 1 else rows[:, g, :d_qk])   # [n, d_qk]
+            V = K[:, :d_v]                                           # [n, d_v]
+            Q = widen_bf16(q[b, h0:h1, :])                           # [h1-h0, d_qk]
+            S = scale * (Q @ K.T)                                    # [h1-h0, n]
+            m = S.max(axis=1, keepdims=True)
+            W = np.exp(S - m)
+            denom = W.sum(axis=1, keepdims=True)
+            out[b, h0 - head_lo:h1 - head_lo] = (W @ V) / denom
+            lse[b, h0 - head_lo:h1 - head_lo] = (m + np.log(denom))[:, 0]
     return out, lse
 
 

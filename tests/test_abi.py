@@ -58,6 +58,8 @@ def _decode_rc(splash, desc, head_lo=0, head_hi=128, tok_lo=0, tok_hi=4096, ptr=
     (dict(d_qk=128, d_v=128), dict(), sp.EUNSUPPORTED),
     (dict(d_v=256), dict(), sp.EUNSUPPORTED),
     (dict(page_size=48), dict(), sp.EUNSUPPORTED),
+    (dict(num_kv_heads=-1), dict(), sp.EINVAL),
+    (dict(num_kv_heads=3), dict(), sp.EINVAL),   # 128 heads do not split over 3 KV heads
     (dict(page_size=8), dict(), sp.EUNSUPPORTED),
     (dict(), dict(ptr=0), sp.EINVAL),
     (dict(), dict(out=0), sp.EINVAL),
@@ -114,6 +116,18 @@ def test_plan_shapes(splash):
     assert sp.decode_plan(16, 128, 576, 512, 64, 1024, 20000, 0.07, 0, 128, 0, 65536)[0] == 16
     # chunks never exceed 128 tiles: one 1M-token request still gets 256 of them
     assert sp.decode_plan(1, 128, 576, 512, 64, 16384, 20000, 0.07, 0, 128, 0, 1 << 20)[0] == 256
+
+
+def test_plan_kv_heads(splash):
+    # G = 2: 64 query heads per KV head -> one 64-head group per launch
+    s, g, w = sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_kv_heads=2)
+    assert g == 1
+    # G = 8: 16 heads per KV head; a slice over two KV heads plans per head
+    s8, g8, w8 = sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 8, 40, 0, 4096, num_kv_heads=8)
+    assert g8 == 1 and w8 > 0
+    # G = 1 and G = 0 are the same single latent head
+    assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_kv_heads=0) == \
+        sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_kv_heads=1)
 
 
 def test_plan_env_override(splash, monkeypatch):

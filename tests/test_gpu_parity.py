@@ -258,6 +258,29 @@ def test_transition_repack_bit_exact(transition):
     assert torch.equal(back[torch.from_numpy(moved).long().to(DEV)], t["kv"][torch.from_numpy(moved).long().to(DEV)])
 
 
+@pytest.mark.parametrize("G,heads,splits", [(2, (0, 128), 0), (4, (0, 128), 0), (8, (0, 128), 0),
+                                            (4, (20, 70), 0), (8, (8, 40), 3), (2, (0, 128), 5)])
+def test_few_kv_heads(G, heads, splits):
+    """G shared latent KV heads (query head h reads KV head h // (H/G)): every
+    head group is its own launch over its KV head's rows of the pool."""
+    c = W.make_decode_case(f"gqa{G}", 50 + G, [700, 1500, 33, 2100], num_heads=128, d_qk=576, d_v=512,
+                           page_size=64, scale=W.LATENT_SCALE, head_lo=heads[0], head_hi=heads[1],
+                           extra_pages=3, num_kv_heads=G)
+    _print(f"case few KV heads G={G} heads={heads} splits={splits}")
+    go, gl = run_decode(c, num_splits=splits)
+    ro, rl = run_oracle(c)
+    assert_close(go, gl, ro, rl, what=f"G={G} heads={heads}")
+
+
+def test_few_kv_heads_tiny():
+    c = W.make_decode_case("gqa_tiny", 60, [17, 64, 5], num_heads=8, d_qk=80, d_v=64, page_size=16,
+                           scale=1.0 / math.sqrt(80.0), std=0.5, head_lo=1, head_hi=7, extra_pages=2, num_kv_heads=2)
+    _print("case few KV heads tiny")
+    go, gl = run_decode(c)
+    ro, rl = run_oracle(c)
+    assert_close(go, gl, ro, rl, what="tiny G=2")
+
+
 def test_background_handoff_concurrent(transition):
     """Decode on one stream while the repack runs in slices on a second
     stream (both default priority), reading the same KV pool: the decode

@@ -120,6 +120,31 @@ def pin_brute_force(decode, merge):
                 assert np.allclose(out[b, h], np.array([float(x) for x in o]), rtol=0, atol=1e-12)
 
 
+def pin_brute_force_kv_heads(decode, merge):
+    """G = 2 and G = 4 shared KV heads (query head h reads KV head h*G // H):
+    50-digit mpmath over the dense logical cache, all heads and a head slice
+    that crosses a group boundary."""
+    for G, H, slice_ in ((2, 8, (0, 8)), (4, 8, (1, 6))):
+        c = W.make_decode_case("gqa", 30 + G, [9, 1, 23], num_heads=H, d_qk=12, d_v=8, page_size=4,
+                               scale=0.37, std=0.7, head_lo=slice_[0], head_hi=slice_[1], extra_pages=2,
+                               keep_dense=True, num_kv_heads=G)
+        out, lse = _run(decode, c)
+        for b in range(c.num_reqs):
+            n = int(c.seq_lens[b])
+            for j, h in enumerate(range(c.head_lo, c.head_hi)):
+                kvh = h * G // H
+                K = [_f64(c.dense_kv[b][t][kvh]) for t in range(n)]
+                qh = _f64(c.q[b, h])
+                with mpmath.workdps(50):
+                    sc = [mpmath.mpf(c.scale) * mpmath.fsum(mpmath.mpf(x) * y for x, y in zip(qh, k)) for k in K]
+                    w = [mpmath.exp(x) for x in sc]
+                    Z = mpmath.fsum(w)
+                    o = [mpmath.fsum(w[i] * K[i][d] for i in range(n)) / Z for d in range(c.d_v)]
+                    L = mpmath.log(Z)
+                assert abs(float(L) - lse[b, j]) <= 1e-12 * max(1.0, abs(float(L)))
+                assert np.allclose(out[b, j], np.array([float(x) for x in o]), rtol=0, atol=1e-12)
+
+
 def pin_layout_invariance(decode, merge):
     """Head slices (TP), token ranges + merge (CP) and request subsets (DP / DOP) equal the whole."""
     c = _small_case(seed=25, lens=(5, 33, 1, 64, 40, 17), H=8)
@@ -217,7 +242,7 @@ def pin_merge_identities(decode, merge):
     assert abs(l2[0] - math.log(4.0)) <= 1e-15
 
 
-ALL_PINS = [pin_one_token, pin_equal_scores, pin_brute_force, pin_layout_invariance,
+ALL_PINS = [pin_one_token, pin_equal_scores, pin_brute_force, pin_brute_force_kv_heads, pin_layout_invariance,
             pin_page_permutation, pin_bounds, pin_empty_range, pin_merge_identities]
 
 
@@ -233,7 +258,7 @@ def test_oracle_pins(pin):
 DECODE_MUTANTS = {
     "dropped scale": ("scale * (Q @ K.T)", "(Q @ K.T)"),
     "V from the rope end": ("V = K[:, :d_v]", "V = K[:, -d_v:]"),
-    "wrong page slot": ("t % page_size, :d_qk", "(t + 1) % page_size, :d_qk"),
+    "wrong page slot": ("rows = kv_pages[pages, t % page_size]", "rows = kv_pages[pages, (t + 1) % page_size]"),
     "wrong page index": ("block_table[b, t // page_size]", "block_table[b, (t + 1) // page_size]"),
     "LSE without the max": ("(m + np.log(denom))", "(np.log(denom))"),
     "sign of the max shift": ("np.exp(S - m)", "np.exp(m - S)"),
@@ -241,6 +266,10 @@ DECODE_MUTANTS = {
     "range end off by one": ("hi = min(int(tok_hi), int(seq_lens[b]))", "hi = min(int(tok_hi), int(seq_lens[b])) - 1"),
     "transposed operand": ("(Q @ K.T)", "(Q[:, ::-1] @ K.T)"),
     "no normalisation": ("(W @ V) / denom", "(W @ V)"),
+    "one KV head for every group": ("rows[:, g, :d_qk]", "rows[:, 0, :d_qk]"),
+    "KV heads in reverse": ("rows[:, g, :d_qk]", "rows[:, G - 1 - g, :d_qk]"),
+    "group boundary off by one": ("max(head_lo, g * group), min(head_hi, (g + 1) * group)",
+                                  "max(head_lo, g * group + 1), min(head_hi, (g + 1) * group + 1)"),
 }
 MERGE_MUTANTS = {
     "merged LSE sign": ("M_safe + np.log(s_safe)", "M_safe - np.log(s_safe)"),

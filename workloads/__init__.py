@@ -79,10 +79,11 @@ class DecodeCase:
     tok_lo: int
     tok_hi: int
     q: np.ndarray            # uint16 [B, H, d_qk]
-    kv_pages: np.ndarray     # uint16 [num_pages, page_size, d_qk]
+    kv_pages: np.ndarray     # uint16 [num_pages, page_size, d_qk], or [.., G, d_qk] with G latent heads
     block_table: np.ndarray  # int32  [B, max_pages_per_req]; -1 = no page
     seq_lens: np.ndarray     # int32  [B]
     dense_kv: Optional[List[np.ndarray]] = None  # per request, logical order (optional)
+    num_kv_heads: int = 1    # G latent KV heads per token; query head h reads head h // (H / G)
 
     @property
     def num_q_heads(self) -> int:
@@ -99,7 +100,8 @@ def make_decode_case(name: str, seed: int, seq_lens, num_heads: int, d_qk: int, 
                      head_lo: int = 0, head_hi: Optional[int] = None,
                      tok_lo: int = 0, tok_hi: Optional[int] = None,
                      extra_pages: int = 0, live_only_in_range: bool = False,
-                     max_pages_per_req: Optional[int] = None, keep_dense: bool = False) -> DecodeCase:
+                     max_pages_per_req: Optional[int] = None, keep_dense: bool = False,
+                     num_kv_heads: int = 1) -> DecodeCase:
     """Build a paged decode case.
 
     Every request gets ceil(len/page_size) physical pages, placed at a random
@@ -109,6 +111,8 @@ def make_decode_case(name: str, seed: int, seq_lens, num_heads: int, d_qk: int, 
     NaN (a share must never read outside its range).  With ``keep_dense`` the
     case also carries each request's rows in logical token order
     (``dense_kv[b]``, uint16 [len_b, d_qk]), drawn before any page placement.
+    With ``num_kv_heads`` G > 1 every token holds G latent rows: the pool is
+    [num_pages, page_size, G, d_qk] (and dense rows [len_b, G, d_qk]).
     """
     gens = _children(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
@@ -125,7 +129,9 @@ def make_decode_case(name: str, seed: int, seq_lens, num_heads: int, d_qk: int, 
     perm = gens[_SEED_PERM].permutation(num_pages).astype(np.int32)
 
     q = _normal_bf16(gens[_SEED_Q], (B, num_heads, d_qk), std)
-    kv = np.full((num_pages, page_size, d_qk), BF16_QNAN, dtype=np.uint16)
+    G = int(num_kv_heads)
+    row_shape = (d_qk,) if G == 1 else (G, d_qk)
+    kv = np.full((num_pages, page_size) + row_shape, BF16_QNAN, dtype=np.uint16)
     block_table = np.full((B, max_pages_per_req), -1, dtype=np.int32)
 
     # Draw the KV values request by request, in logical order, so that the
@@ -144,18 +150,19 @@ def make_decode_case(name: str, seed: int, seq_lens, num_heads: int, d_qk: int, 
             used = min(page_size, n - t0)
             if live_only_in_range and (t0 + page_size <= tok_lo or t0 >= tok_hi):
                 if keep_dense:
-                    rows.append(np.full((used, d_qk), BF16_QNAN, dtype=np.uint16))
+                    rows.append(np.full((used,) + row_shape, BF16_QNAN, dtype=np.uint16))
                 continue
-            vals = _normal_bf16(kv_gen, (used, d_qk), std)
-            kv[phys, :used, :] = vals
+            vals = _normal_bf16(kv_gen, (used,) + row_shape, std)
+            kv[phys, :used] = vals
             if keep_dense:
                 rows.append(vals)
         if keep_dense:
-            dense.append(np.concatenate(rows, axis=0) if rows else np.zeros((0, d_qk), np.uint16))
+            dense.append(np.concatenate(rows, axis=0) if rows else np.zeros((0,) + row_shape, np.uint16))
     return DecodeCase(name=name, seed=seed, num_reqs=B, num_heads=num_heads, d_qk=d_qk, d_v=d_v,
                       page_size=page_size, max_pages_per_req=max_pages_per_req, num_pages=num_pages,
                       scale=scale, head_lo=head_lo, head_hi=head_hi, tok_lo=tok_lo, tok_hi=tok_hi,
-                      q=q, kv_pages=kv, block_table=block_table, seq_lens=seq_lens, dense_kv=dense)
+                      q=q, kv_pages=kv, block_table=block_table, seq_lens=seq_lens, dense_kv=dense,
+                      num_kv_heads=G)
 
 
 def loguniform_lengths(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
@@ -180,10 +187,11 @@ def case_tiny(seed: int = 1, keep_dense: bool = False) -> DecodeCase:
                             scale=1.0 / math.sqrt(80.0), std=0.5, extra_pages=2, keep_dense=keep_dense)
 
 
-def case_owner(seed: int = 2, B: int = 16, ctx: int = 4096) -> DecodeCase:
-    """Request-owned share (DP-attention / DOP owner): B x ctx tokens, all 128 heads."""
+def case_owner(seed: int = 2, B: int = 16, ctx: int = 4096, num_kv_heads: int = 1) -> DecodeCase:
+    """Request-owned share (DP-attention / DOP owner): B x ctx tokens, all 128 heads
+    (over num_kv_heads shared latent KV heads)."""
     return make_decode_case("owner", seed, [ctx] * B, num_heads=128, d_qk=LATENT_QK, d_v=LATENT_V,
-                            page_size=64, scale=LATENT_SCALE)
+                            page_size=64, scale=LATENT_SCALE, num_kv_heads=num_kv_heads)
 
 
 def case_tp(seed: int = 3, B: int = 16, ctx: int = 16384, heads=(0, 16)) -> DecodeCase:
@@ -209,9 +217,12 @@ def case_transition(seed: int = 5, n: int = 64, lo: int = 512, hi: int = 65536) 
 
 
 def sweep_case(share: str, ctx: int, seed: int = 6, B: int = 16) -> DecodeCase:
-    """The B=16 input-length sweep, one rank's share: 'owner', 'tp' or 'cp' (rank 3 of 8)."""
+    """The B=16 input-length sweep, one rank's share: 'owner', 'tp' or 'cp' (rank 3 of 8);
+    'gqa<G>' is the owner share over G shared latent KV heads."""
     if share == "owner":
         return case_owner(seed=seed, B=B, ctx=ctx)
+    if share.startswith("gqa"):
+        return case_owner(seed=seed, B=B, ctx=ctx, num_kv_heads=int(share[3:]))
     if share == "tp":
         return case_tp(seed=seed, B=B, ctx=ctx)
     if share == "cp":
