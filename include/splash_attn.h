@@ -93,8 +93,8 @@ typedef struct splash_desc {
  * The work is split into KV chunks (split-KV) when the share is too small to
  * fill the GPU; partials then go to a library-owned workspace (allocated on
  * first need, grown on demand, freed by splash_release_workspace) and are
- * merged on the same stream.  With G > 1 the heads of each KV head the share
- * touches are one such launch (and merge), in order on the stream.
+ * merged on the same stream.  Every KV head the share touches is served by
+ * the same launch (one decode kernel, plus one merge kernel when split).
  * Growing the workspace synchronises the device,
  * so a call that needs more workspace must not be made under stream capture.
  * Errors: SPLASH_EINVAL for null pointers, non-positive sizes, head range
@@ -156,7 +156,8 @@ int splash_release_workspace(void);
 /*
  * The launch plan splash_decode_attn would use for this share, without
  * launching anything (a pure host function): split-KV chunks per request,
- * workgroups per (request, chunk) along the heads, and workspace bytes.
+ * workgroups per (request, chunk) along the heads (over all KV heads the
+ * share touches), and workspace bytes.
  * Returns the same validation status as splash_decode_attn.
  */
 int splash_decode_plan(const splash_desc* desc, int32_t head_lo, int32_t head_hi, int32_t tok_lo,

@@ -132,8 +132,11 @@ int page_shift_of(int ps) {
 
 struct Plan {
   DecodeVariant variant;
-  int head_groups;      // workgroups along the heads
+  int head_groups;      // workgroups along the heads (KV heads touched x z_per_kv)
   int heads_per_group;  // 32 * wh
+  int kv_group;         // query heads per KV head
+  int kv_first;         // first KV head the share touches
+  int z_per_kv;         // head groups per KV head
   int grid_splits;      // blockIdx.x extent
   int fixed_splits;     // > 0: every request cut into this many chunks
   int chunk_tiles;      // otherwise: 32-token tiles per chunk
@@ -193,11 +196,20 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
   int rc = validate_decode(d, head_lo, head_hi, tok_lo, tok_hi);
   if (rc) return rc;
   const int hs = head_hi - head_lo;
+  // KV heads the share touches, and the most query heads any one of them serves
+  const int group = d->num_heads / kv_heads_of(d);
+  const int kv_first = head_lo / group, kv_last = (head_hi - 1) / group;
+  int slice = 0;
+  for (int g = kv_first; g <= kv_last; ++g) {
+    const int lo = head_lo > g * group ? head_lo : g * group;
+    const int hi = head_hi < (g + 1) * group ? head_hi : (g + 1) * group;
+    if (hi - lo > slice) slice = hi - lo;
+  }
   const int wv_max = d->d_v / 32 >= 4 ? 4 : d->d_v / 32;
   // Heads per workgroup: 32 (4 waves split the V columns), 64 (2 head
   // groups x 2 column halves) or 128 (4 head groups).  SPLASH_WG_HEADS
   // overrides the choice (tuning).
-  int wg_heads = hs <= 32 ? 32 : (hs <= 64 ? 64 : 128);
+  int wg_heads = slice <= 32 ? 32 : (slice <= 64 ? 64 : 128);
   if (const char* env = getenv("SPLASH_WG_HEADS")) {
     const int v = atoi(env);
     if (v == 32 || v == 64 || v == 128) wg_heads = v;
@@ -210,7 +222,11 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
     p->variant = {d->d_qk, d->d_v, 4, 1};
   }
   p->heads_per_group = 32 * p->variant.wh;
-  p->head_groups = (hs + p->heads_per_group - 1) / p->heads_per_group;
+  p->kv_group = group;
+  p->kv_first = kv_first;
+  p->z_per_kv = (slice + p->heads_per_group - 1) / p->heads_per_group;
+  p->head_groups = (kv_last - kv_first + 1) * p->z_per_kv;
+  if (p->head_groups > 65535) return fail(SPLASH_EINVAL, "too many head groups (%d)", p->head_groups);
 
   // Longest token range any request can have in this share.
   const int64_t cap = (int64_t)d->max_pages_per_req * d->page_size;
@@ -283,23 +299,9 @@ int splash_decode_plan(const splash_desc* desc, int32_t head_lo, int32_t head_hi
   Plan p;
   int rc = make_plan(desc, head_lo, head_hi, tok_lo, tok_hi, &p);
   if (rc) return rc;
-  // per KV head: the first one's split and head-group counts; the largest
-  // workspace (the launches run in order and share it)
-  const int group = desc->num_heads / kv_heads_of(desc);
-  int64_t ws = 0;
-  bool first = true;
-  for (int g = head_lo / group; g * group < head_hi; ++g) {
-    const int lo = head_lo > g * group ? head_lo : g * group;
-    const int hi = head_hi < (g + 1) * group ? head_hi : (g + 1) * group;
-    Plan pg;
-    if ((rc = make_plan(desc, lo, hi, tok_lo, tok_hi, &pg))) return rc;
-    if (first) p = pg;
-    first = false;
-    if (pg.workspace_bytes > ws) ws = pg.workspace_bytes;
-  }
   if (num_splits) *num_splits = p.grid_splits;
   if (head_groups) *head_groups = p.head_groups;
-  if (workspace_bytes) *workspace_bytes = ws;
+  if (workspace_bytes) *workspace_bytes = p.workspace_bytes;
   return SPLASH_OK;
 }
 
@@ -308,14 +310,11 @@ int splash_decode_plan(const splash_desc* desc, int32_t head_lo, int32_t head_hi
 namespace splash {
 namespace {
 
-// Decode attention of the heads [head_lo, head_hi) that share one latent KV
-// head: `kv` points at that head's row of token 0 of page 0, `kv_row` is the
-// pool's elements per token (G * d_qk), and the results go to heads
-// [out_head0, out_head0 + hs) of out / lse rows of out_heads heads.
-int decode_one_kv_head(const splash_desc* desc, const void* q, const uint16_t* kv, int32_t kv_row,
-                       const int32_t* block_table, const int32_t* seq_lens, int32_t head_lo, int32_t head_hi,
-                       int32_t tok_lo, int32_t tok_hi, float* out, float* lse, int32_t out_heads,
-                       int32_t out_head0, int dev, int32_t* dev_err, hipStream_t stream) {
+// Decode attention of the share's heads [head_lo, head_hi): one decode
+// launch over every KV head the share touches (and one merge when split).
+int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, const int32_t* block_table,
+                 const int32_t* seq_lens, int32_t head_lo, int32_t head_hi, int32_t tok_lo, int32_t tok_hi,
+                 float* out, float* lse, int dev, int32_t* dev_err, hipStream_t stream) {
   Plan p;
   int rc = make_plan(desc, head_lo, head_hi, tok_lo, tok_hi, &p);
   if (rc) return rc;
@@ -324,12 +323,15 @@ int decode_one_kv_head(const splash_desc* desc, const void* q, const uint16_t* k
   DecodeArgs a{};
   a.q = (const uint16_t*)q;
   a.kv = kv;
+  a.kv_group = p.kv_group;
+  a.kv_first = p.kv_first;
+  a.z_per_kv = p.z_per_kv;
   a.bt = block_table;
   a.seq_lens = seq_lens;
   a.dev_err = dev_err;
   a.q_req_stride = (int64_t)desc->num_heads * desc->d_qk;
-  a.kv_row = kv_row;
-  a.page_stride = (int64_t)desc->page_size * kv_row;
+  a.kv_row = kv_heads_of(desc) * desc->d_qk;
+  a.page_stride = (int64_t)desc->page_size * a.kv_row;
   a.max_pages = desc->max_pages_per_req;
   a.num_pages = desc->num_pages;
   a.page_shift = page_shift_of(desc->page_size);
@@ -347,18 +349,12 @@ int decode_one_kv_head(const splash_desc* desc, const void* q, const uint16_t* k
     a.lse = lse;
     a.out_split_stride = 0;
     a.lse_split_stride = 0;
-    a.out_heads = out_heads;
-    a.out_head0 = out_head0;
     a.partial_out = 0;
     hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
     if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
     return SPLASH_OK;
   }
-  // split-KV: partials in the workspace (rows of this launch's hs heads),
-  // then the merge writes the caller's rows
-  a.out_heads = hs;
-  a.out_head0 = 0;
-  const MergeOut om{hs, out_heads, out_head0};
+  // split-KV: partials in the workspace, then the merge writes the caller's rows
   void* ws;
   if ((rc = ensure_workspace(dev, (size_t)p.workspace_bytes, &ws))) return rc;
   const int64_t rows = (int64_t)desc->num_reqs * hs;
@@ -383,7 +379,7 @@ int decode_one_kv_head(const splash_desc* desc, const void* q, const uint16_t* k
     if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
     e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
       return launch_lse_merge_segmented(part_o, part_l, req_info, (int32_t)rows, hs, desc->d_v, out, lse, stream, e0,
-                                        e1, om);
+                                        e1);
     });
     if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
     return SPLASH_OK;
@@ -398,7 +394,7 @@ int decode_one_kv_head(const splash_desc* desc, const void* q, const uint16_t* k
   hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
   if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
   e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
-    return launch_lse_merge(part_o, part_l, p.grid_splits, (int32_t)rows, desc->d_v, out, lse, stream, e0, e1, om);
+    return launch_lse_merge(part_o, part_l, p.grid_splits, (int32_t)rows, desc->d_v, out, lse, stream, e0, e1);
   });
   if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
   return SPLASH_OK;
@@ -420,25 +416,13 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
   if ((((uintptr_t)q) & 15) || (((uintptr_t)kv_pages) & 15) || (((uintptr_t)out) & 15))
     return fail(SPLASH_EINVAL, "q, kv_pages and out must be 16-byte aligned");
   if (desc->num_reqs == 0) return SPLASH_OK;
-  const int hs = head_hi - head_lo;
-  const int G = kv_heads_of(desc);
-  const int group = desc->num_heads / G;
-
   int dev;
   if ((rc = current_device(&dev))) return rc;
   std::lock_guard<std::mutex> lock(g_mu);
   int32_t* dev_err;
   if ((rc = device_error_word(dev, &dev_err))) return rc;
-  // one launch (decode, and merge when split) per KV head the share touches
-  for (int g = head_lo / group; g * group < head_hi; ++g) {
-    const int lo = head_lo > g * group ? head_lo : g * group;
-    const int hi = head_hi < (g + 1) * group ? head_hi : (g + 1) * group;
-    rc = decode_one_kv_head(desc, q, (const uint16_t*)kv_pages + (int64_t)g * desc->d_qk, G * desc->d_qk,
-                            block_table, seq_lens, lo, hi, tok_lo, tok_hi, out, lse, hs, lo - head_lo, dev, dev_err,
-                            stream);
-    if (rc) return rc;
-  }
-  return SPLASH_OK;
+  return decode_share(desc, q, (const uint16_t*)kv_pages, block_table, seq_lens, head_lo, head_hi, tok_lo, tok_hi,
+                      out, lse, dev, dev_err, stream);
 }
 
 int splash_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows, int32_t d_v,

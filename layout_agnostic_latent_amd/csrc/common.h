@@ -11,7 +11,7 @@ namespace splash {
 // Arguments of one decode-attention launch (passed by value to the kernel).
 struct DecodeArgs {
   const uint16_t* q;         // bf16 [B][H][d_qk]
-  const uint16_t* kv;        // bf16 [num_pages][page_size][d_qk]
+  const uint16_t* kv;        // bf16 [num_pages][page_size][G][d_qk] (G = 1: [num_pages][page_size][d_qk])
   const int32_t* bt;         // int32 [B][max_pages]
   const int32_t* seq_lens;   // int32 [B]
   float* out;                // fp32 [splits][B][Hs][d_v] (splits = 1: the caller's output)
@@ -19,9 +19,7 @@ struct DecodeArgs {
   int32_t* dev_err;          // library device error word
   int64_t q_req_stride;      // H * d_qk
   int64_t page_stride;       // page_size * kv_row
-  int32_t kv_row;            // elements per token in the pool: G * d_qk (kv points at this launch's KV head)
-  int32_t out_heads;         // heads per request row of out / lse (their row stride)
-  int32_t out_head0;         // out / lse head of this launch's first head
+  int32_t kv_row;            // elements per token in the pool: G * d_qk
   int64_t out_split_stride;  // B * Hs * d_v
   int64_t lse_split_stride;  // B * Hs
   int32_t max_pages;
@@ -29,6 +27,12 @@ struct DecodeArgs {
   int32_t page_shift;        // log2(page_size)
   int32_t head_lo;
   int32_t n_heads;           // Hs = head_hi - head_lo
+  // Shared KV heads: query head h reads KV head h / kv_group.  blockIdx.z is
+  // (KV head kv_first + z / z_per_kv, head group z % z_per_kv of that KV
+  // head's part of the share).
+  int32_t kv_group;          // query heads per KV head (H / G)
+  int32_t kv_first;          // first KV head the share touches
+  int32_t z_per_kv;          // head groups per KV head
   int32_t tok_lo;
   int32_t tok_hi;
   int32_t fixed_splits;      // > 0: every request is cut into this many chunks
@@ -62,17 +66,9 @@ struct DecodeVariant {
 hipError_t launch_decode(const DecodeVariant& v, dim3 grid, const DecodeArgs& a, hipStream_t stream,
                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
-// Output rows of a merge: row r = (b, h) with b = r / hs, h = r % hs goes to
-// out row b * out_heads + out_head0 + h (the identity when out_heads = hs
-// and out_head0 = 0).
-struct MergeOut {
-  int32_t hs, out_heads, out_head0;
-};
-
 hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows,
                             int32_t d_v, float* out, float* lse_out, hipStream_t stream,
-                            hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
-                            MergeOut om = MergeOut{0, 0, 0});
+                            hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // Work-list mode handles batches of up to this many requests.
 constexpr int kPlanMaxReqs = 8192;
@@ -81,8 +77,7 @@ constexpr int kPlanMaxReqs = 8192;
 // req_info[b] (rows = B * hs).
 hipError_t launch_lse_merge_segmented(const float* partials, const float* lses, const int4* req_info, int32_t rows,
                                       int32_t hs, int32_t d_v, float* out, float* lse_out, hipStream_t stream,
-                                      hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
-                                      MergeOut om = MergeOut{0, 0, 0});
+                                      hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_kv_repack(const void* src, const int32_t* src_table, void* dst, const int32_t* dst_table,
                             int64_t n_pairs, int64_t page_bytes, int32_t src_num_pages,

@@ -272,8 +272,16 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     split = item.w;
   }
   const int b_out = worklist ? 0 : b;  // request term of the output row index
-  const int hs = (blockIdx.z * WH + wh) * 32 + n;  // head index within the share
-  const bool head_ok = hs < a.n_heads;
+  // this workgroup's KV head and its query heads [k_lo, k_hi) within the share
+  const int zk = blockIdx.z / a.z_per_kv;
+  const int zz = blockIdx.z - zk * a.z_per_kv;
+  const int kvh = a.kv_first + zk;
+  const int k_lo = max(a.head_lo, kvh * a.kv_group) - a.head_lo;
+  const int k_hi = min(a.head_lo + a.n_heads, (kvh + 1) * a.kv_group) - a.head_lo;
+  const uint16_t* kv = a.kv + (int64_t)kvh * D_QK;
+  const int head0 = k_lo + (zz * WH + wh) * 32;  // first head of this wave within the share
+  const int hs = head0 + n;                      // this lane's head within the share
+  const bool head_ok = hs < k_hi;
   const int hs_safe = head_ok ? hs : 0;
 
   // Read-only tables through the constant address space: scalar loads, so
@@ -300,9 +308,9 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   const int mlo = max(lo, t_begin * kTileTok);
   const int mhi = min(hi, t_end * kTileTok);
 
-  float* out_row = a.out + split * a.out_split_stride + ((int64_t)b_out * a.out_heads + a.out_head0 + hs_safe) * D_V;
+  float* out_row = a.out + split * a.out_split_stride + ((int64_t)b_out * a.n_heads + hs_safe) * D_V;
   float* lse_ptr =
-      a.lse ? a.lse + split * a.lse_split_stride + (int64_t)b_out * a.out_heads + a.out_head0 + hs_safe : nullptr;
+      a.lse ? a.lse + split * a.lse_split_stride + (int64_t)b_out * a.n_heads + hs_safe : nullptr;
 
   if (t_end <= t_begin) {  // empty chunk: O = 0, LSE = -inf
     // A split-KV partial with LSE = -inf is never read by the merge, so only
@@ -400,8 +408,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   auto dma_plan = [&](int t, int slot, TilePages pg) -> DmaPlan {
     const int tok0 = t * kTileTok;
     DmaPlan d;
-    d.base0 = (const char*)(a.kv + (int64_t)pg.p0 * a.page_stride + (int64_t)(tok0 & ps_mask) * a.kv_row);
-    d.base1 = (const char*)(a.kv + (int64_t)pg.p1 * a.page_stride) - 16 * row_b;
+    d.base0 = (const char*)(kv + (int64_t)pg.p0 * a.page_stride + (int64_t)(tok0 & ps_mask) * a.kv_row);
+    d.base1 = (const char*)(kv + (int64_t)pg.p1 * a.page_stride) - 16 * row_b;
     d.lds = smem_base + slot * C::TILE_B;
     d.rlo = max(mlo - tok0, 0);
     d.rhi1 = min(mhi - tok0, kTileTok) - 1;
@@ -583,20 +591,32 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   };
 
   // One pipelined step: scores of tile `it` are in `s`; the output update of
-  // tile it-1 (weights `pprev`) runs while tile it's softmax is computed:
-  // after MFMAs 0-3 partial row maxima, after MFMA 4 the new running max,
-  // after MFMAs 5-20 one probability each (pairs packed to bf16).
+  // tile it-1 (weights `pprev`) runs while tile it's softmax is computed in
+  // slices between its MFMAs.  The wave issues in order, so a slice whose
+  // instructions depend on each other would hold back the next MFMA by the
+  // whole chain's latency; every slice therefore only uses values computed
+  // in earlier slices (at least one MFMA, 32 cycles, ago):
+  //   slices 0-6: the row max (a max3 tree, then the other half's max),
+  //   7-9:        scaled max and the new running max,
+  //   10-28:      a three-stage pipeline over the 16 scores: exponent,
+  //               exp2, then the sum and the bf16 pair packing.
   auto pv_and_softmax = [&](int it, floatx16& s, bf16x8 (&pprev)[2], bf16x8 (&vring)[PV_PF], auto with_dma,
                             const DmaPlan& dp, auto&& extra) {
     mask_tile(s, it);
-    float mpart[4];
+    float mx[4];
     float m_new = m_run;
+    const float thr = m_run + kRescaleThreshold;
     bool need = false;
     uint32_t pw[2][4];
-    float lsum = 0.0f, lrsum = 0.0f, pf_even = 0.0f;
+    float lsum = 0.0f, lrsum = 0.0f;
     // `pin` ties a value to its slice: pure arithmetic would otherwise be
     // sunk past the scheduling barriers to the end of the block.
     auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
+    auto max3 = [](float x, float y, float z) {
+      float r;
+      asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+      return r;
+    };
     auto step = [&](int i) {
       extra(i);
       if constexpr (decltype(with_dma)::value && C::DMA_QK < C::DMA_W) {
@@ -605,35 +625,70 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
         for (int k = 0; k < ND; ++k)
           if ((k * C::NM) / ND == i) issue_one(dp, C::DMA_QK + k);
       }
-      if (i < 4) {
-        mpart[i] = fmaxf(fmaxf(s[4 * i], s[4 * i + 1]), fmaxf(s[4 * i + 2], s[4 * i + 3]));
-        pin(mpart[i]);
+      if (i == 0) {
+        mx[0] = max3(s[0], s[1], s[2]);
+        mx[1] = max3(s[3], s[4], s[5]);
+      } else if (i == 1) {
+        mx[2] = max3(s[6], s[7], s[8]);
+        mx[3] = max3(s[9], s[10], s[11]);
+      } else if (i == 2) {
+        mx[0] = max3(mx[0], mx[1], s[15]);
+        mx[1] = max3(s[12], s[13], s[14]);
+      } else if (i == 3) {
+        mx[0] = max3(mx[0], mx[2], mx[3]);
       } else if (i == 4) {
-        const float mloc = max_across_halves(fmaxf(fmaxf(mpart[0], mpart[1]), fmaxf(mpart[2], mpart[3]))) * a.scale_log2;
-        need = mloc > m_run + kRescaleThreshold;
-        m_new = need ? mloc : m_run;
+        mx[0] = max3(mx[0], mx[1], mx[1]);
+      } else if (i == 5) {
+        // both halves of the head's column: lane l and lane l ^ 32
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[0]), __float_as_uint(mx[0]), false, false);
+        mx[1] = __uint_as_float(r[0]);
+        mx[2] = __uint_as_float(r[1]);
+        pin(mx[1]);
+        pin(mx[2]);
+      } else if (i == 6) {
+        mx[0] = max3(mx[1], mx[2], mx[2]);
+      } else if (i == 7) {
+        mx[0] *= a.scale_log2;
+        pin(mx[0]);
+      } else if (i == 8) {
+        need = mx[0] > thr;
+      } else if (i == 9) {
+        m_new = need ? mx[0] : m_run;
         pin(m_new);
-      } else if (i < 5 + 16) {
-        const int e = i - 5;
-        float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.scale_log2, -m_new));
-        lsum += pf;
-        pin(lsum);
-        if (e & 1) {
-          const bf16x2 pair = {(__bf16)pf_even, (__bf16)pf};
+      } else if (i < 10 + 19) {
+        const int t = i - 10;
+        if (t < 16) {
+          float x = __builtin_fmaf(s[t], a.scale_log2, -m_new);
+          pin(x);
+          s[t] = x;
+        }
+        if (t >= 1 && t <= 16) {
+          float x = __builtin_amdgcn_exp2f(s[t - 1]);
+          pin(x);
+          s[t - 1] = x;
+        }
+        if (t >= 2 && t <= 17) {
+          lsum += s[t - 2];
+          pin(lsum);
+        }
+        if (t >= 3 && t <= 17 && ((t - 2) & 1)) {  // pack p[e-1], p[e] (e = t-2 odd)
+          const int e = t - 2;
+          const bf16x2 pair = {(__bf16)s[e - 1], (__bf16)s[e]};
           uint32_t w = __builtin_bit_cast(uint32_t, pair);
           asm volatile("" : "+v"(w));
           pw[e >> 3][(e & 7) >> 1] = w;
-          lrsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lrsum, false);
+        }
+        if (t >= 4 && t <= 18 && ((t - 3) & 1)) {  // sum of the rounded pair packed one slice ago
+          const int e = t - 3;
+          lrsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e >> 3][(e & 7) >> 1]), ones, lrsum,
+                                                  false);
           pin(lrsum);
-        } else {
-          pf_even = pf;
-          pin(pf_even);
         }
       }
     };
     pv_tile(it - 1, pprev, vring, step);
     // slices beyond the MFMA count (variants with fewer V blocks)
-    constexpr int kSteps = 5 + 16 > kPlanStep + 1 ? 5 + 16 : kPlanStep + 1;
+    constexpr int kSteps = 10 + 19 > kPlanStep + 1 ? 10 + 19 : kPlanStep + 1;
 #pragma unroll
     for (int i = C::NM; i < kSteps; ++i) step(i);
     const bool any_need = __any(need);
@@ -785,8 +840,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   __syncthreads();
   {
     float* stage = (float*)smem + wave * 32 * C::PITCH;
-    const int head0 = (blockIdx.z * WH + wh) * 32;  // first head of this wave within the share
-    float* out_base = a.out + split * a.out_split_stride + ((int64_t)b_out * a.out_heads + a.out_head0 + head0) * D_V;
+    float* out_base = a.out + split * a.out_split_stride + ((int64_t)b_out * a.n_heads + head0) * D_V;
     constexpr int ROWF = C::PB * 32;  // staged floats per row and pass
 #pragma unroll
     for (int pass = 0; pass < C::VB / C::PB; ++pass) {
@@ -805,7 +859,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
         const int e = (i * 64 + lane) * 4;
         const int row = e / ROWF, col = e % ROWF;
         const floatx4 v = *(const floatx4*)(stage + row * C::PITCH + col);
-        if (head0 + row < a.n_heads) *(floatx4*)(out_base + (int64_t)row * D_V + col0 + col) = v;
+        if (head0 + row < k_hi) *(floatx4*)(out_base + (int64_t)row * D_V + col0 + col) = v;
       }
     }
   }

@@ -70,7 +70,7 @@ template <typename Parts>
 __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* __restrict__ P,
                                                                   const float* __restrict__ L, Parts parts,
                                                                   int32_t d_v, float* __restrict__ out,
-                                                                  float* __restrict__ lse_out, MergeOut om) {
+                                                                  float* __restrict__ lse_out) {
   __shared__ float w_s[kLdsParts];
   __shared__ floatx4 acc_s[kMergeThreads];
   __shared__ float red[kMergeThreads / 64];
@@ -79,8 +79,7 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
   const auto rp = parts.at(row);
   const int n = rp.n;
   const int c4n = d_v >> 2;
-  const int64_t orow_i = om.hs > 0 ? (row / om.hs) * om.out_heads + om.out_head0 + row % om.hs : row;
-  floatx4* orow = (floatx4*)(out + orow_i * d_v);
+  floatx4* orow = (floatx4*)(out + (int64_t)row * d_v);
 
   float m = -INFINITY;
   for (int p = tid; p < n; p += kMergeThreads) {
@@ -91,7 +90,7 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
   const float M = block_max(m, red);
   if (M == -INFINITY) {  // no live part (NaN LSEs also end here: fmaxf ignores them)
     for (int c = tid; c < c4n; c += kMergeThreads) orow[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (lse_out && tid == 0) lse_out[orow_i] = -INFINITY;
+    if (lse_out && tid == 0) lse_out[row] = -INFINITY;
     return;
   }
   float sum = 0.0f;
@@ -132,26 +131,26 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
       orow[c] = acc;
     }
   }
-  if (lse_out && tid == 0) lse_out[orow_i] = lse;
+  if (lse_out && tid == 0) lse_out[row] = lse;
 }
 
 }  // namespace
 
 hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows,
                             int32_t d_v, float* out, float* lse_out, hipStream_t stream, hipEvent_t e0,
-                            hipEvent_t e1, MergeOut om) {
+                            hipEvent_t e1) {
   if (rows == 0) return hipSuccess;
   hipExtLaunchKernelGGL(lse_merge_kernel<UniformParts>, dim3(rows), dim3(kMergeThreads), 0, stream, e0, e1, 0,
-                        partials, lses, UniformParts{n_parts, rows}, d_v, out, lse_out, om);
+                        partials, lses, UniformParts{n_parts, rows}, d_v, out, lse_out);
   return hipGetLastError();
 }
 
 hipError_t launch_lse_merge_segmented(const float* partials, const float* lses, const int4* req_info, int32_t rows,
                                       int32_t hs, int32_t d_v, float* out, float* lse_out, hipStream_t stream,
-                                      hipEvent_t e0, hipEvent_t e1, MergeOut om) {
+                                      hipEvent_t e0, hipEvent_t e1) {
   if (rows == 0) return hipSuccess;
   hipExtLaunchKernelGGL(lse_merge_kernel<ListedParts>, dim3(rows), dim3(kMergeThreads), 0, stream, e0, e1, 0,
-                        partials, lses, ListedParts{req_info, hs}, d_v, out, lse_out, om);
+                        partials, lses, ListedParts{req_info, hs}, d_v, out, lse_out);
   return hipGetLastError();
 }
 

@@ -119,12 +119,17 @@ def test_plan_shapes(splash):
 
 
 def test_plan_kv_heads(splash):
-    # G = 2: 64 query heads per KV head -> one 64-head group per launch
+    # G = 2: 64 query heads per KV head -> one 64-head workgroup per KV head
     s, g, w = sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_kv_heads=2)
-    assert g == 1
-    # G = 8: 16 heads per KV head; a slice over two KV heads plans per head
+    assert g == 2
+    # G = 8: 16 heads per KV head; heads [8, 40) touch KV heads 0, 1 and 2
     s8, g8, w8 = sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 8, 40, 0, 4096, num_kv_heads=8)
-    assert g8 == 1 and w8 > 0
+    assert g8 == 3 and w8 > 0
+    # G = 4 over all heads: 32 heads per KV head, four workgroups along the heads
+    assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_kv_heads=4)[1] == 4
+    # a slice inside one KV head plans like G = 1 with that slice
+    assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 64, 96, 0, 4096, num_kv_heads=2) == \
+        sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 64, 96, 0, 4096)
     # G = 1 and G = 0 are the same single latent head
     assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_kv_heads=0) == \
         sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_kv_heads=1)

@@ -261,8 +261,9 @@ def test_transition_repack_bit_exact(transition):
 @pytest.mark.parametrize("G,heads,splits", [(2, (0, 128), 0), (4, (0, 128), 0), (8, (0, 128), 0),
                                             (4, (20, 70), 0), (8, (8, 40), 3), (2, (0, 128), 5)])
 def test_few_kv_heads(G, heads, splits):
-    """G shared latent KV heads (query head h reads KV head h // (H/G)): every
-    head group is its own launch over its KV head's rows of the pool."""
+    """G shared latent KV heads (query head h reads KV head h // (H/G)): one
+    launch serves every KV head the share touches, each workgroup reading its
+    KV head's rows of the pool."""
     c = W.make_decode_case(f"gqa{G}", 50 + G, [700, 1500, 33, 2100], num_heads=128, d_qk=576, d_v=512,
                            page_size=64, scale=W.LATENT_SCALE, head_lo=heads[0], head_hi=heads[1],
                            extra_pages=3, num_kv_heads=G)
