@@ -53,6 +53,9 @@ extern "C" {
 /* Device error bits (splash_device_errors). */
 #define SPLASH_DEVERR_BAD_PAGE 1      /* decode: block-table entry outside [0, num_pages) */
 #define SPLASH_DEVERR_REPACK_PAIR 2   /* repack: a pair was rejected (see splash_kv_repack) */
+#define SPLASH_DEVERR_PARTIAL_RANGE 4 /* decode: a split-KV partial output value exceeded the fp16
+                                         range (|x| > 65504) and was clamped; the merged output of
+                                         that request is inexact */
 
 /* Shape of a paged latent-KV decode batch. */
 typedef struct splash_desc {
@@ -93,7 +96,9 @@ typedef struct splash_desc {
  * The work is split into KV chunks (split-KV) when the share is too small to
  * fill the GPU; partials then go to a library-owned workspace (allocated on
  * first need, grown on demand, freed by splash_release_workspace) and are
- * merged on the same stream.  Every KV head the share touches is served by
+ * merged on the same stream.  A partial output is kept in fp16 (its LSE in
+ * fp32) between the two kernels; a value beyond the fp16 range is clamped and
+ * raises SPLASH_DEVERR_PARTIAL_RANGE.  Every KV head the share touches is served by
  * the same launch (one decode kernel, plus one merge kernel when split).
  * Growing the workspace synchronises the device,
  * so a call that needs more workspace must not be made under stream capture.

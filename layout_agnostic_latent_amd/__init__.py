@@ -18,14 +18,14 @@ from typing import Optional, Tuple
 
 __all__ = ["LIB_PATH", "SplashError", "lib", "decode_attn", "decode_plan", "lse_merge", "kv_repack",
            "device_errors", "release_workspace", "profile_start", "profile_stop", "DEVERR_BAD_PAGE",
-           "DEVERR_REPACK_PAIR"]
+           "DEVERR_REPACK_PAIR", "DEVERR_PARTIAL_RANGE"]
 
 # The in-tree build; SPLASH_LIB may name another build of the same library.
 LIB_PATH = os.environ.get("SPLASH_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                          "libsplash_attn.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
-DEVERR_BAD_PAGE, DEVERR_REPACK_PAIR = 1, 2
+DEVERR_BAD_PAGE, DEVERR_REPACK_PAIR, DEVERR_PARTIAL_RANGE = 1, 2, 4
 
 
 class SplashError(RuntimeError):

@@ -149,7 +149,8 @@ struct Plan {
 };
 
 // Work-list workspace layout (byte offsets; every part 256-byte aligned):
-// partial outputs and LSEs per work item, then each request's part list.
+// partial outputs (fp16) and LSEs (fp32) per work item, then each request's
+// part list.
 struct WorklistLayout {
   int64_t part_o, part_l, req_info, total;
 };
@@ -157,10 +158,23 @@ int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 WorklistLayout worklist_layout(int64_t items, int64_t B, int64_t hs, int64_t d_v) {
   WorklistLayout w;
   w.part_o = 0;
-  w.part_l = align256(w.part_o + items * hs * d_v * (int64_t)sizeof(float));
+  w.part_l = align256(w.part_o + items * hs * d_v * (int64_t)sizeof(uint16_t));
   w.req_info = align256(w.part_l + items * hs * (int64_t)sizeof(float));
   w.total = align256(w.req_info + B * 16);
   return w;
+}
+
+// Grid-mode workspace: fp16 partial outputs [splits][rows][d_v], then fp32
+// LSEs [splits][rows].
+struct GridLayout {
+  int64_t part_o, part_l, total;
+};
+GridLayout grid_layout(int64_t splits, int64_t rows, int64_t d_v) {
+  GridLayout g;
+  g.part_o = 0;
+  g.part_l = align256(splits * rows * d_v * (int64_t)sizeof(uint16_t));
+  g.total = align256(g.part_l + splits * rows * (int64_t)sizeof(float));
+  return g;
 }
 
 // Latent KV heads of the pool (0 in the descriptor means one).
@@ -268,7 +282,7 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
   if (p->grid_splits == 1) {
     p->workspace_bytes = 0;
   } else if (forced > 0 || d->num_reqs > kPlanMaxReqs) {
-    p->workspace_bytes = (int64_t)p->grid_splits * d->num_reqs * hs * (d->d_v + 1) * (int64_t)sizeof(float);
+    p->workspace_bytes = grid_layout(p->grid_splits, (int64_t)d->num_reqs * hs, d->d_v).total;
   } else {
     // Requests may be shorter than the table's capacity (ragged batches):
     // the kernel cuts the chunks from seq_lens.  Full chunks number
@@ -361,7 +375,7 @@ int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, con
   if (p.worklist) {
     const WorklistLayout w = worklist_layout(p.items_max, desc->num_reqs, hs, desc->d_v);
     char* base = (char*)ws;
-    float* part_o = (float*)(base + w.part_o);
+    uint16_t* part_o = (uint16_t*)(base + w.part_o);
     float* part_l = (float*)(base + w.part_l);
     int4* req_info = (int4*)(base + w.req_info);
     a.num_reqs = desc->num_reqs;
@@ -369,7 +383,7 @@ int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, con
     a.plan_min_chunk = 4;
     a.plan_max_chunk = kMaxChunkTiles;
     a.req_info = req_info;
-    a.out = part_o;
+    a.out = (float*)part_o;  // fp16 partials (partial_out = 1)
     a.lse = part_l;
     a.out_split_stride = (int64_t)hs * desc->d_v;
     a.lse_split_stride = hs;
@@ -378,15 +392,16 @@ int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, con
     hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, wgrid, a, stream, e0, e1); });
     if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
     e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
-      return launch_lse_merge_segmented(part_o, part_l, req_info, (int32_t)rows, hs, desc->d_v, out, lse, stream, e0,
-                                        e1);
+      return launch_split_merge_segmented(part_o, part_l, req_info, (int32_t)rows, hs, desc->d_v, out, lse, stream,
+                                          e0, e1);
     });
     if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
     return SPLASH_OK;
   }
-  float* part_o = (float*)ws;
-  float* part_l = part_o + (int64_t)p.grid_splits * rows * desc->d_v;
-  a.out = part_o;
+  const GridLayout gl = grid_layout(p.grid_splits, rows, desc->d_v);
+  uint16_t* part_o = (uint16_t*)((char*)ws + gl.part_o);
+  float* part_l = (float*)((char*)ws + gl.part_l);
+  a.out = (float*)part_o;  // fp16 partials (partial_out = 1)
   a.lse = part_l;
   a.out_split_stride = rows * desc->d_v;
   a.lse_split_stride = rows;
@@ -394,7 +409,7 @@ int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, con
   hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
   if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
   e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
-    return launch_lse_merge(part_o, part_l, p.grid_splits, (int32_t)rows, desc->d_v, out, lse, stream, e0, e1);
+    return launch_split_merge(part_o, part_l, p.grid_splits, (int32_t)rows, desc->d_v, out, lse, stream, e0, e1);
   });
   if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
   return SPLASH_OK;

@@ -8,13 +8,19 @@
 
 namespace splash {
 
+// Device error bits (the SPLASH_DEVERR_* values of the public header).
+constexpr int32_t kDevErrBadPage = 1;
+constexpr int32_t kDevErrRepackPair = 2;
+constexpr int32_t kDevErrPartialRange = 4;
+
 // Arguments of one decode-attention launch (passed by value to the kernel).
 struct DecodeArgs {
   const uint16_t* q;         // bf16 [B][H][d_qk]
   const uint16_t* kv;        // bf16 [num_pages][page_size][G][d_qk] (G = 1: [num_pages][page_size][d_qk])
   const int32_t* bt;         // int32 [B][max_pages]
   const int32_t* seq_lens;   // int32 [B]
-  float* out;                // fp32 [splits][B][Hs][d_v] (splits = 1: the caller's output)
+  float* out;                // fp32 [B][Hs][d_v], the caller's output (partial_out = 0), or
+                             // fp16 [splits][B][Hs][d_v] split-KV partials (partial_out = 1)
   float* lse;                // fp32 [splits][B][Hs], may be null when splits = 1
   int32_t* dev_err;          // library device error word
   int64_t q_req_stride;      // H * d_qk
@@ -37,7 +43,7 @@ struct DecodeArgs {
   int32_t tok_hi;
   int32_t fixed_splits;      // > 0: every request is cut into this many chunks
   int32_t chunk_tiles;       // fixed_splits == 0: 32-token tiles per chunk
-  int32_t partial_out;       // 1: out/lse are split-KV partials (merged afterwards)
+  int32_t partial_out;       // 1: out/lse are split-KV partials (merged afterwards); out holds fp16
   // Work-list mode (plan_target > 0): the chunks are cut from the device's
   // seq_lens inside the kernel.  Every workgroup computes the plan (one
   // chunk length for the batch so that its total tiles fill about
@@ -75,6 +81,17 @@ constexpr int kPlanMaxReqs = 8192;
 
 // Merge of the work-list partials: row (b, h) combines the parts listed in
 // req_info[b] (rows = B * hs).
+// Merge of split-KV partials (fp16 O, fp32 LSE) into the caller's fp32
+// rows: uniform parts at p * rows + row, or the parts listed per request.
+// d_v a multiple of 8, at most 512.
+hipError_t launch_split_merge(const uint16_t* partials, const float* lses, int32_t n_parts, int32_t rows,
+                              int32_t d_v, float* out, float* lse_out, hipStream_t stream,
+                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+hipError_t launch_split_merge_segmented(const uint16_t* partials, const float* lses, const int4* req_info,
+                                        int32_t rows, int32_t hs, int32_t d_v, float* out, float* lse_out,
+                                        hipStream_t stream, hipEvent_t ev_start = nullptr,
+                                        hipEvent_t ev_stop = nullptr);
+
 hipError_t launch_lse_merge_segmented(const float* partials, const float* lses, const int4* req_info, int32_t rows,
                                       int32_t hs, int32_t d_v, float* out, float* lse_out, hipStream_t stream,
                                       hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);

@@ -45,14 +45,16 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 constexpr int kPageLds = 4096;  // page ids of a chunk staged in LDS (16 KiB)
 constexpr int kVPages = 4;      // VGPRs of page ids per lane: chunks of up to 256 pages
 constexpr int kLdsBytes = 160 * 1024 - kPageLds * 4;
 constexpr int kMaxBuf = 4;
-constexpr float kRescaleThreshold = 8.0f;
-constexpr int kPlanStep = 22;  // PV MFMA after which the next tile's DMA plan is made (past the softmax slices)  // log2 units: p = exp2(s - m) stays <= 256
+constexpr float kHalfMax = 65504.0f;  // largest finite fp16 (split-KV partials are stored in fp16)
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = exp2(s - m) stays <= 256
+constexpr int kPlanStep = 22;  // PV MFMA after which the next tile's DMA plan is made (past the softmax slices)
 
 // LDS tile layout ("slabs"): the 16-byte chunk c of tile row r lives at
 //   (c / 8) * SLAB_B + r * 128 + ((c % 8) ^ row_swizzle(r)) * 16,
@@ -721,15 +723,28 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   const std::integral_constant<bool, true> kDma;
   const std::integral_constant<bool, false> kNoDma;
 
-  // Prologue: tiles 0 and 1 in flight (two ring slots stay free for the
-  // tiles being computed), issued before anything else the chunk loads.
+  // Prologue.  Order of issue: the chunk's page ids, Q, then the first two
+  // tiles' DMA.  The Q loads touch 32 rows per instruction and so keep the
+  // texture addresser busy for a while; the page-id loads, issued first,
+  // land meanwhile, so the DMA needs no block-table fetch of its own.  Q and
+  // tile 0 are waited for at iteration 0 (tile 1 stays in flight: it is
+  // the youngest vector-memory work).
+
+  // The chunk's block-table entries [j0, j1] are loaded once, so that the
+  // tile loop issues no scalar-memory loads: an outstanding scalar load
+  // would make every LDS-read wait in the loop a full drain of the counter
+  // the two share.  Up to 64 * kVPages pages go to VGPRs, up to kPageLds to
+  // LDS; longer chunks read the table through the scalar cache.
+  const int32_t* bt_src = a.bt + (int64_t)b * a.max_pages + j0;
+  if (pt_vgpr) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    if (i < ntiles) {
-      const DmaPlan d = dma_plan(t_begin + i, i, pages_of(t_begin + i));
-#pragma unroll
-      for (int k = 0; k < C::DMA_W; ++k) issue_one(d, k);
-    }
+    for (int k = 0; k < kVPages; ++k) vpg[k] = j0 + 64 * k + lane <= j1 ? bt_src[64 * k + lane] : 0;
+  } else if (pt_lds) {
+    for (int j = threadIdx.x; j <= j1 - j0; j += C::NTHREADS) page_lds[j] = bt_src[j];
+    __syncthreads();
+    pt_mode = 2;
+  }
+  asm volatile("" ::: "memory");
 
   // ---- Q for this wave's 32 heads: B operand of every score MFMA ----
   {
@@ -741,34 +756,24 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
       for (int s = 0; s < C::KS; ++s) qf[s] = bf16x8{};
     }
   }
-
-  // The chunk's block-table entries [j0, j1] are loaded once, so that the
-  // tile loop issues no scalar-memory loads: an outstanding scalar load
-  // would make every LDS-read wait in the loop a full drain of the counter
-  // the two share.  Up to 64 * kVPages pages go to VGPRs, up to kPageLds to
-  // LDS; longer chunks read the table through the scalar cache.  (The first
-  // two tiles' DMA, issued above, read their pages through the scalar cache,
-  // so that their HBM latency overlaps the Q loads and this setup.)
-  {
-    const int32_t* src = a.bt + (int64_t)b * a.max_pages + j0;
-    if (pt_vgpr) {
+  asm volatile("" ::: "memory");
+  if (pt_vgpr) {
+    // the page ids are complete here (the compiler waits for them, not for
+    // the younger Q loads), so the loop never waits on them
 #pragma unroll
-      for (int k = 0; k < kVPages; ++k) vpg[k] = j0 + 64 * k + lane <= j1 ? src[64 * k + lane] : 0;
-#pragma unroll
-      for (int k = 0; k < kVPages; ++k) asm volatile("" ::"v"(vpg[k]));
-      pt_mode = 1;
-    } else if (pt_lds) {
-      for (int j = threadIdx.x; j <= j1 - j0; j += C::NTHREADS) page_lds[j] = src[j];
-      __syncthreads();
-      pt_mode = 2;
-    }
+    for (int k = 0; k < kVPages; ++k) asm volatile("" ::"v"(vpg[k]));
+    pt_mode = 1;
   }
 
-  // Make the Q loads complete here, visibly to the compiler, so that it
-  // places no vector-memory waits inside the tile loop (those would also
-  // drain the KV prefetch, which the counter tracks too).
+  // Tiles 0 and 1 in flight (two ring slots stay free for the tiles being
+  // computed).
 #pragma unroll
-  for (int s = 0; s < C::KS; ++s) asm volatile("" ::"v"(qf[s]));
+  for (int i = 0; i < 2; ++i)
+    if (i < ntiles) {
+      const DmaPlan d = dma_plan(t_begin + i, i, pages_of(t_begin + i));
+#pragma unroll
+      for (int k = 0; k < C::DMA_W; ++k) issue_one(d, k);
+    }
 
   // Iteration 0: scores and softmax of tile 0 (the output is still zero, so
   // the running max is simply set).  Tile 2's DMA goes into its free slot.
@@ -779,10 +784,14 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     else wait_vmcnt<0>();
     __syncthreads();
     dp = dma_plan(t_begin + 2, 2 % C::NBUF, pages_of(t_begin + min(2, ntiles - 1)));
-    floatx16 s = qk_tile(0, kDma, 2 < ntiles, dp, [](int) {});
-    if (2 < ntiles) {  // the DMAs that later iterations issue between PV MFMAs
+    // The compiler waits for each Q operand at its MFMA, counting only its
+    // own loads: with tile 1's DMA younger than Q, the last of those waits
+    // also drain tile 1.  Tile 2's DMA is therefore issued after the scores,
+    // not between them (it would be drained too).
+    floatx16 s = qk_tile(0, kNoDma, false, dp, [](int) {});
+    if (2 < ntiles) {
 #pragma unroll
-      for (int k = C::DMA_QK; k < C::DMA_W; ++k) issue_one(dp, k);
+      for (int k = 0; k < C::DMA_W; ++k) issue_one(dp, k);
     }
     mask_tile(s, 0);
     m_run = tile_max(s);
@@ -827,7 +836,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   }
   // let the last PV MFMAs retire before the epilogue reads the accumulators
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
-  if (bad_page && lane == 0) atomicOr(a.dev_err, 1);
+  if (bad_page && lane == 0) atomicOr(a.dev_err, kDevErrBadPage);
 
   // ---- epilogue: normalise and store ----
   // The accumulators hold, per lane, 16-byte pieces of 32 different output
@@ -837,6 +846,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float lr_tot = lr_run + __shfl_xor(lr_run, 32, 64);
   const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
+  float amax = 0.0f;  // largest |partial output| this lane stores (fp16 range check)
   __syncthreads();
   {
     float* stage = (float*)smem + wave * 32 * C::PITCH;
@@ -854,15 +864,37 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
           *(floatx4*)(stage + n * C::PITCH + vbl * 32 + rq * 8 + 4 * g) = v;
         }
       const int col0 = (wv * C::VB + pass * C::PB) * 32;
+      if (!a.partial_out) {
 #pragma unroll
-      for (int i = 0; i < 32 * ROWF / 256; ++i) {
-        const int e = (i * 64 + lane) * 4;
-        const int row = e / ROWF, col = e % ROWF;
-        const floatx4 v = *(const floatx4*)(stage + row * C::PITCH + col);
-        if (head0 + row < k_hi) *(floatx4*)(out_base + (int64_t)row * D_V + col0 + col) = v;
+        for (int i = 0; i < 32 * ROWF / 256; ++i) {
+          const int e = (i * 64 + lane) * 4;
+          const int row = e / ROWF, col = e % ROWF;
+          const floatx4 v = *(const floatx4*)(stage + row * C::PITCH + col);
+          if (head0 + row < k_hi) *(floatx4*)(out_base + (int64_t)row * D_V + col0 + col) = v;
+        }
+      } else {
+        // split-KV partial: fp16, 16 bytes per lane (8 columns).  A value
+        // beyond the fp16 range is clamped to it and flagged.
+        _Float16* hbase = (_Float16*)a.out + split * a.out_split_stride + ((int64_t)b_out * a.n_heads + head0) * D_V;
+#pragma unroll
+        for (int i = 0; i < 32 * ROWF / 512; ++i) {
+          const int e = (i * 64 + lane) * 8;
+          const int row = e / ROWF, col = e % ROWF;
+          const floatx4 v0 = *(const floatx4*)(stage + row * C::PITCH + col);
+          const floatx4 v1 = *(const floatx4*)(stage + row * C::PITCH + col + 4);
+          halfx8 h;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float x = k < 4 ? v0[k] : v1[k - 4];
+            amax = fmaxf(amax, fabsf(x));
+            h[k] = (_Float16)__builtin_amdgcn_fmed3f(x, -kHalfMax, kHalfMax);
+          }
+          if (head0 + row < k_hi) *(halfx8*)(hbase + (int64_t)row * D_V + col0 + col) = h;
+        }
       }
     }
   }
+  if (__any(amax > kHalfMax) && lane == 0) atomicOr(a.dev_err, kDevErrPartialRange);
   if (head_ok && lse_ptr && wv == 0 && g == 0)
     *lse_ptr = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
 }

@@ -28,7 +28,7 @@ __global__ void __launch_bounds__(kRepackThreads) kv_repack_kernel(const uint8_t
   if (s < 0 || d < 0 || s >= ns || d >= nd) {
     if (threadIdx.x == 0) {
       if (err_count) atomicAdd(err_count, 1);
-      atomicOr(dev_err, 2);
+      atomicOr(dev_err, kDevErrRepackPair);
     }
     return;
   }

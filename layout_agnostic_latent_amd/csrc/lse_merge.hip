@@ -134,7 +134,94 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
   if (lse_out && tid == 0) lse_out[row] = lse;
 }
 
+// Split-KV merge: one wave per output row, each lane 8 columns.  The LSEs
+// and fp16 partial rows of up to kSplitBatch parts are loaded in one round
+// (no address depends on a loaded value: a part with LSE -inf, whose row the
+// decode kernel never wrote, is read but given no weight), then combined,
+// with an online rescale of the sums when a row has more parts.  No LDS and
+// no barrier: the row's cost is one round trip to memory.
+constexpr int kSplitBatch = 16;
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+template <typename Parts>
+__global__ void __launch_bounds__(256) split_merge_kernel(const _Float16* __restrict__ P, const float* __restrict__ L,
+                                                          Parts parts, int32_t rows, int32_t d_v,
+                                                          float* __restrict__ out, float* __restrict__ lse_out) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  const auto rp = parts.at(row);
+  const int n = rp.n;
+  const int c = lane * 8;
+  const bool active = c < d_v;
+  float M = -INFINITY, S = 0.0f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < n; p0 += kSplitBatch) {
+    float l[kSplitBatch];
+    halfx8 v[kSplitBatch];
+#pragma unroll
+    for (int u = 0; u < kSplitBatch; ++u) {
+      const bool live = p0 + u < n;
+      const int64_t pi = live ? rp.index(p0 + u) : 0;
+      l[u] = live ? L[pi] : -INFINITY;
+      v[u] = (live && active) ? *(const halfx8*)(P + pi * d_v + c) : halfx8{};
+    }
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < kSplitBatch; ++u) mb = fmaxf(mb, l[u]);
+    if (mb == -INFINITY) continue;  // no live part so far
+    const float sc = __expf(M - mb);  // 0 while M is -inf
+    S *= sc;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] *= sc;
+#pragma unroll
+    for (int u = 0; u < kSplitBatch; ++u) {
+      if (l[u] != -INFINITY) {
+        const float w = __expf(l[u] - mb);
+        S += w;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] += w * (float)v[u][k];
+      }
+    }
+    M = mb;
+  }
+  floatx4* orow = (floatx4*)(out + row * d_v + c);
+  if (M == -INFINITY) {  // every part empty
+    if (active) {
+      orow[0] = floatx4{0.f, 0.f, 0.f, 0.f};
+      orow[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (lse_out && lane == 0) lse_out[row] = -INFINITY;
+    return;
+  }
+  const float inv = 1.0f / S;
+  if (active) {
+    orow[0] = floatx4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    orow[1] = floatx4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  }
+  if (lse_out && lane == 0) lse_out[row] = M + __logf(S);
+}
+
 }  // namespace
+
+hipError_t launch_split_merge(const uint16_t* partials, const float* lses, int32_t n_parts, int32_t rows,
+                              int32_t d_v, float* out, float* lse_out, hipStream_t stream, hipEvent_t e0,
+                              hipEvent_t e1) {
+  if (rows == 0) return hipSuccess;
+  hipExtLaunchKernelGGL(split_merge_kernel<UniformParts>, dim3((rows + 3) / 4), dim3(256), 0, stream, e0, e1, 0,
+                        (const _Float16*)partials, lses, UniformParts{n_parts, rows}, rows, d_v, out, lse_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_merge_segmented(const uint16_t* partials, const float* lses, const int4* req_info,
+                                        int32_t rows, int32_t hs, int32_t d_v, float* out, float* lse_out,
+                                        hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  if (rows == 0) return hipSuccess;
+  hipExtLaunchKernelGGL(split_merge_kernel<ListedParts>, dim3((rows + 3) / 4), dim3(256), 0, stream, e0, e1, 0,
+                        (const _Float16*)partials, lses, ListedParts{req_info, hs}, rows, d_v, out, lse_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows,
                             int32_t d_v, float* out, float* lse_out, hipStream_t stream, hipEvent_t e0,

@@ -94,13 +94,14 @@ def test_plan_shapes(splash):
     # request-owned, 128 heads, 4,096 tokens: one head group, split to fill 256 CUs
     s, g, w = sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096)
     # unforced splits are cut on the device from the real lengths: room for
-    # 256 full chunks plus one remainder per request, each a 128 x 513
-    # partial, plus each request's 16-byte part list
+    # 256 full chunks plus one remainder per request, each a 128 x 512 fp16
+    # partial output and 128 fp32 LSEs, plus each request's 16-byte part list
     assert g == 1 and s == 16
-    assert 272 * 128 * 513 * 4 + 16 * 16 <= w <= 272 * 128 * 513 * 4 + 4096
-    # forced splits
+    per_item = 128 * 512 * 2 + 128 * 4
+    assert 272 * per_item + 16 * 16 <= w <= 272 * per_item + 4096
+    # forced splits: fp16 outputs, then fp32 LSEs (each part 256-byte aligned)
     s, g, w = sp.decode_plan(16, 128, 576, 512, 64, 256, 4096, 0.07, 0, 16, 0, 16384, num_splits=8)
-    assert s == 8 and g == 1 and w == 8 * 16 * 16 * 513 * 4
+    assert s == 8 and g == 1 and w == 8 * 16 * 16 * 512 * 2 + 8 * 16 * 16 * 4
     # a 64-head slice uses 32-head x 2 waves groups
     s, g, _ = sp.decode_plan(2, 128, 576, 512, 64, 8, 16, 0.07, 0, 64, 0, 512)
     assert g == 1

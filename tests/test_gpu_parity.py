@@ -401,6 +401,29 @@ def test_bad_page_index_is_flagged_not_faulted():
     assert sp.device_errors(clear=True) & sp.DEVERR_BAD_PAGE
 
 
+def test_partial_range_is_clamped_and_flagged():
+    """Split-KV partial outputs are kept in fp16.  V values near 1e5 (q scaled
+    down by the same factor, so the scores keep their N(0,1)-input scale): a
+    call without splits keeps fp32 throughout and matches the oracle; with
+    splits the partials exceed the fp16 range, are clamped (finite) and raise
+    the device error bit."""
+    c = W.make_decode_case("big_v", 45, [700, 300], num_heads=128, d_qk=576, d_v=512, page_size=64,
+                           scale=W.LATENT_SCALE)
+    f = 1e5
+    kv = c.kv_pages.copy()
+    kv[..., :c.d_v] = W.bf16_bits((kv[..., :c.d_v].astype(np.uint32) << 16).view(np.float32) * f)
+    q = W.bf16_bits((c.q.astype(np.uint32) << 16).view(np.float32) / f)
+    c2 = W.DecodeCase(**{**c.__dict__, "kv_pages": kv, "q": q})
+    sp.device_errors(clear=True)
+    go, gl = run_decode(c2, num_splits=1)
+    assert not sp.device_errors(clear=True) & sp.DEVERR_PARTIAL_RANGE
+    ro, rl = run_oracle(c2)
+    assert_close(go / f, gl, ro / f, rl, what="V near 1e5, no split")
+    gs, _ = run_decode(c2, num_splits=4)
+    assert sp.device_errors(clear=True) & sp.DEVERR_PARTIAL_RANGE
+    assert np.all(np.isfinite(gs)) and np.abs(gs).max() <= 65504.0
+
+
 def test_merge_edges():
     rows, d_v = 5, 512
     P = torch.randn((3, rows, d_v), dtype=torch.float32, device=DEV)
