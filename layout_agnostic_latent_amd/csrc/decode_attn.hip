@@ -232,7 +232,7 @@ struct Cfg {
   static constexpr int KS = D_QK / 16;               // K-steps of the score MFMA
   static constexpr int VB = D_V / 32 / WV;           // 32-wide V blocks per wave
   static constexpr int NM = 2 * VB;                  // PV MFMAs per tile: (k-step, V block)
-  static constexpr int KPF = KS < 4 ? KS : 4;        // K operands in flight (score MFMAs)
+  static constexpr int KPF = KS < 4 ? KS : 4;        // K operands in flight (score MFMAs; <= KSW)
   static constexpr int VPF = NM < 4 ? NM : 4;        // V operands in flight (PV MFMAs)
   // DMA instructions of the next tile issued between the score MFMAs; the
   // rest go between the PV MFMAs.
@@ -240,7 +240,18 @@ struct Cfg {
   static constexpr int PB = VB < 8 ? VB : 8;         // V blocks per epilogue pass
   static constexpr int PITCH = PB * 32 + 4;          // floats per staged output row (+16 B: banks)
   static constexpr int STAGE_B = NW * 32 * PITCH * 4;  // epilogue staging bytes
-  static constexpr int SMEM_B = NBUF * TILE_B > STAGE_B ? NBUF * TILE_B : STAGE_B;
+  // Split score contraction (one head group, four waves splitting V): wave w
+  // computes the scores over k-steps w, w+4, ..., and the four partial
+  // score tiles are summed through LDS, instead of every wave computing
+  // the whole tile.  The exchange area takes the page-id area's place.
+  static constexpr bool KSPLIT = WH == 1 && WV == 4 && KS % 4 == 0;
+  static constexpr int KSW = KSPLIT ? KS / 4 : KS;   // k-steps of the score MFMAs per wave
+  static constexpr int RING_B = NBUF * TILE_B;
+  static constexpr int XCH_B = KSPLIT ? 4 * 16 * 64 * 4 : 0;  // four 32x32 fp32 partial tiles
+  static constexpr int PAGE_LDS = KSPLIT ? 0 : kPageLds;     // page ids staged in LDS
+  static constexpr int BODY_B = RING_B + XCH_B > STAGE_B ? RING_B + XCH_B : STAGE_B;
+  static constexpr int SMEM_B = BODY_B + PAGE_LDS * 4;       // + the page-id area
+  static_assert(SMEM_B <= 160 * 1024, "LDS");
   static_assert(D_QK % 16 == 0 && D_V % (32 * WV) == 0 && D_V <= D_QK, "shape");
   static_assert(DMA_T % NW == 0, "DMA split");
   static_assert(NBUF == 4, "LDS ring: two tiles computed, two in flight");
@@ -252,7 +263,9 @@ template <int D_QK, int D_V, int WH, int WV>
 __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const DecodeArgs a) {
   using C = Cfg<D_QK, D_V, WH, WV>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_B];
-  __shared__ __attribute__((aligned(16))) int32_t page_lds[kPageLds];  // this chunk's physical page ids
+  // this chunk's physical page ids; with the split score contraction only
+  // the plan's scratch, in the (then unused) exchange area
+  int32_t* const page_lds = (int32_t*)(smem + (C::KSPLIT ? C::RING_B : C::BODY_B));
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -331,7 +344,10 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   }
   const int ntiles = t_end - t_begin;
 
-  bf16x8 qf[C::KS];  // Q of this wave's 32 heads (loaded after the first DMAs)
+  bf16x8 qf[C::KSW];  // Q of this wave's 32 heads, its k-steps (loaded in the prologue)
+  // first k-step of this wave; its k-steps are ks0 + KS/KSW * s
+  const int ks0 = C::KSPLIT ? wave : 0;
+  constexpr int KST = C::KS / C::KSW;
   const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   const int ps_mask = (1 << a.page_shift) - 1;
   const int row_b = a.kv_row * 2;  // bytes from one token's row to the next in the pool
@@ -351,7 +367,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // (page j0 + 64k + l in lane l of vpg[k]; read with v_readlane, no memory
   // access and no wait in the loop), 2 = LDS (chunks with more pages).
   const bool pt_vgpr = j1 - j0 < 64 * kVPages;
-  const bool pt_lds = j1 - j0 < kPageLds;
+  const bool pt_lds = j1 - j0 < C::PAGE_LDS;
   int pt_mode = 0;
   int32_t vpg[kVPages];
   // Physical page of token `tok`.
@@ -455,6 +471,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   uint32_t kofs[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) kofs[j] = n * 128 + 16 * ((2u * j + g) ^ row_swizzle(n));
+  // split contraction: this wave's k-steps all have k-step % 4 = wave
+  const uint32_t kofs_w = n * 128 + 16 * ((2u * (uint32_t)ks0 + g) ^ row_swizzle(n));
   //  V^T (A operand of PV) via ds_read_b64_tr_b16: lane (j, q) of each
   //  16-lane group reads row r = 16ks + 8h + 4g + j at column 32*vbg + 16*mh + 4q,
   //  chunk c = 4*vbg + 2*mh + q/2, slab vbg/2.  With x = j>>1 and
@@ -485,26 +503,54 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // K operands are read PF steps ahead of the MFMA that consumes them.  With
   // `with_dma`, the DMA of a later tile (plan `dp`) is issued between the
   // MFMAs, so its issue cost hides behind matrix work.
+  // With the split contraction the wave's partial tile (its k-steps) goes
+  // through LDS and every wave returns the same full tile, summed in one
+  // order.
+  auto kaddr = [&](int s) -> uint32_t {  // LDS offset of this wave's k-step s within a tile
+    if constexpr (C::KSPLIT) return kofs_w + C::SLAB_B * s;  // k-step 4s + wave: slab s
+    else return kofs[s & 3] + C::SLAB_B * (s >> 2);
+  };
   auto qk_tile = [&](int it, auto with_dma, bool do_dma, const DmaPlan& dp, auto&& hook) -> floatx16 {
     const char* tile = smem + (it % C::NBUF) * C::TILE_B;
-    constexpr int PF = C::KPF;
+    constexpr int PF = C::KPF < C::KSW ? C::KPF : C::KSW;
     floatx16 sacc;
     bf16x8 kring[PF];
 #pragma unroll
-    for (int s = 0; s < PF; ++s) kring[s] = *(const bf16x8*)(tile + kofs[s & 3] + C::SLAB_B * (s >> 2));
+    for (int s = 0; s < PF; ++s) kring[s] = *(const bf16x8*)(tile + kaddr(s));
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
+    for (int s = 0; s < C::KSW; ++s) {
       const bf16x8 kf = kring[s % PF];
       if (s == 0) mfma_vgpr_first(sacc, kf, qf[0]);
-      else if (s == C::KS - 1) mfma_vgpr_last(sacc, kf, qf[s]);
+      else if (s == C::KSW - 1) mfma_vgpr_last(sacc, kf, qf[s]);
       else mfma_vgpr(sacc, kf, qf[s]);
-      if (s + PF < C::KS) kring[s % PF] = *(const bf16x8*)(tile + kofs[(s + PF) & 3] + C::SLAB_B * ((s + PF) >> 2));
+      if (s + PF < C::KSW) kring[s % PF] = *(const bf16x8*)(tile + kaddr(s + PF));
       if constexpr (decltype(with_dma)::value) {
 #pragma unroll
         for (int i = 0; i < C::DMA_QK; ++i)
-          if ((i * C::KS) / C::DMA_QK == s && do_dma) issue_one(dp, i);
+          if ((i * C::KSW) / C::DMA_QK == s && do_dma) issue_one(dp, i);
       }
       hook(s);
+    }
+    if constexpr (C::KSPLIT) {
+      // partial tiles, lane-major: element 4q..4q+3 of lane l of wave w at
+      // ((w * 4 + q) * 64 + l) * 16 bytes
+      char* xch = smem + C::RING_B;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(floatx4*)(xch + ((wave * 4 + q) * 64 + lane) * 16) =
+            floatx4{sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+      __syncthreads();
+      floatx4 part[4][4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) part[w][q] = *(const floatx4*)(xch + ((w * 4 + q) * 64 + lane) * 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 t = ((part[0][q] + part[1][q]) + part[2][q]) + part[3][q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc[4 * q + e] = t[e];
+      }
     }
     return sacc;
   };
@@ -587,7 +633,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // reads of tile `it` after the last PV_PF score MFMAs.
   auto vprefetch_hook = [&](int it, bf16x8 (&vring)[PV_PF]) {
     return [&, it](int sidx) {
-      const int i = sidx - (C::KS - PV_PF);
+      const int i = sidx - (C::KSW - PV_PF);
       if (i >= 0) vring[i] = vread(it, i);
     };
   };
@@ -750,10 +796,10 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   {
     const uint16_t* qp = a.q + (int64_t)b * a.q_req_stride + (int64_t)(a.head_lo + hs_safe) * D_QK + 8 * g;
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
+    for (int s = 0; s < C::KSW; ++s) qf[s] = *(const bf16x8*)(qp + 16 * (ks0 + KST * s));
     if (!head_ok) {
 #pragma unroll
-      for (int s = 0; s < C::KS; ++s) qf[s] = bf16x8{};
+      for (int s = 0; s < C::KSW; ++s) qf[s] = bf16x8{};
     }
   }
   asm volatile("" ::: "memory");
