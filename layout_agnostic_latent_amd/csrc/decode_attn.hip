@@ -240,12 +240,13 @@ struct Cfg {
   static constexpr int PB = VB < 8 ? VB : 8;         // V blocks per epilogue pass
   static constexpr int PITCH = PB * 32 + 4;          // floats per staged output row (+16 B: banks)
   static constexpr int STAGE_B = NW * 32 * PITCH * 4;  // epilogue staging bytes
-  // Split score contraction (one head group, four waves splitting V): wave w
-  // computes the scores over k-steps w, w+4, ..., and the four partial
-  // score tiles are summed through LDS, instead of every wave computing
-  // the whole tile.  The exchange area takes the page-id area's place.
-  static constexpr bool KSPLIT = WH == 1 && WV == 4 && KS % 4 == 0;
-  static constexpr int KSW = KSPLIT ? KS / 4 : KS;   // k-steps of the score MFMAs per wave
+  // Split score contraction (the WV > 1 waves of a head group split V's
+  // columns, so each would otherwise compute the same score tile): wave
+  // (wh, wv) computes the scores over k-steps wv, wv + WV, ..., and the WV
+  // partial tiles of a head group are summed through LDS.  The exchange
+  // area takes the page-id area's place.
+  static constexpr bool KSPLIT = WV > 1 && NW == 4 && KS % WV == 0;
+  static constexpr int KSW = KSPLIT ? KS / WV : KS;  // k-steps of the score MFMAs per wave
   static constexpr int RING_B = NBUF * TILE_B;
   static constexpr int XCH_B = KSPLIT ? 4 * 16 * 64 * 4 : 0;  // four 32x32 fp32 partial tiles
   static constexpr int PAGE_LDS = KSPLIT ? 0 : kPageLds;     // page ids staged in LDS
@@ -345,8 +346,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   const int ntiles = t_end - t_begin;
 
   bf16x8 qf[C::KSW];  // Q of this wave's 32 heads, its k-steps (loaded in the prologue)
-  // first k-step of this wave; its k-steps are ks0 + KS/KSW * s
-  const int ks0 = C::KSPLIT ? wave : 0;
+  // first k-step of this wave; its k-steps are ks0 + KST * s
+  const int ks0 = C::KSPLIT ? wv : 0;
   constexpr int KST = C::KS / C::KSW;
   const uint32_t smem_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   const int ps_mask = (1 << a.page_shift) - 1;
@@ -471,8 +472,14 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   uint32_t kofs[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) kofs[j] = n * 128 + 16 * ((2u * j + g) ^ row_swizzle(n));
-  // split contraction: this wave's k-steps all have k-step % 4 = wave
-  const uint32_t kofs_w = n * 128 + 16 * ((2u * (uint32_t)ks0 + g) ^ row_swizzle(n));
+  // split contraction: this wave's k-step s is ks0 + KST * s, at in-slab
+  // chunk pair (ks0 + KST * s) % 4 of slab (ks0 + KST * s) / 4; with
+  // KST = 2 or 4 the pair cycles through 4 / KST values
+  constexpr int KPAIRS = C::KSPLIT ? 4 / KST : 1;
+  uint32_t kofs_w[KPAIRS];
+#pragma unroll
+  for (int t = 0; t < KPAIRS; ++t)
+    kofs_w[t] = n * 128 + 16 * ((2u * (uint32_t)(ks0 + KST * t) + g) ^ row_swizzle(n));
   //  V^T (A operand of PV) via ds_read_b64_tr_b16: lane (j, q) of each
   //  16-lane group reads row r = 16ks + 8h + 4g + j at column 32*vbg + 16*mh + 4q,
   //  chunk c = 4*vbg + 2*mh + q/2, slab vbg/2.  With x = j>>1 and
@@ -507,7 +514,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // through LDS and every wave returns the same full tile, summed in one
   // order.
   auto kaddr = [&](int s) -> uint32_t {  // LDS offset of this wave's k-step s within a tile
-    if constexpr (C::KSPLIT) return kofs_w + C::SLAB_B * s;  // k-step 4s + wave: slab s
+    if constexpr (C::KSPLIT) return kofs_w[s % KPAIRS] + C::SLAB_B * (s / KPAIRS);
     else return kofs[s & 3] + C::SLAB_B * (s >> 2);
   };
   auto qk_tile = [&](int it, auto with_dma, bool do_dma, const DmaPlan& dp, auto&& hook) -> floatx16 {
@@ -540,14 +547,17 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
         *(floatx4*)(xch + ((wave * 4 + q) * 64 + lane) * 16) =
             floatx4{sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
       __syncthreads();
-      floatx4 part[4][4];
+      // the head group's waves are wh + WH * v, v < WV; summed in v order
+      floatx4 part[WV][4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
+      for (int v = 0; v < WV; ++v)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) part[w][q] = *(const floatx4*)(xch + ((w * 4 + q) * 64 + lane) * 16);
+        for (int q = 0; q < 4; ++q) part[v][q] = *(const floatx4*)(xch + (((wh + WH * v) * 4 + q) * 64 + lane) * 16);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const floatx4 t = ((part[0][q] + part[1][q]) + part[2][q]) + part[3][q];
+        floatx4 t = part[0][q];
+#pragma unroll
+        for (int v = 1; v < WV; ++v) t = t + part[v][q];
 #pragma unroll
         for (int e = 0; e < 4; ++e) sacc[4 * q + e] = t[e];
       }
