@@ -43,7 +43,7 @@ def kernel_source_hash() -> str:
 
 
 def short(name: str) -> str:
-    for key in ("decode_attn_kernel", "lse_merge_kernel", "kv_repack_kernel"):
+    for key in ("decode_attn_kernel", "lse_merge_kernel", "split_merge_kernel", "kv_repack_kernel"):
         if key in name:
             i = name.find("<")
             j = name.find(">", i)
