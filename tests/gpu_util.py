@@ -60,6 +60,14 @@ def assert_close(go, gl, ro, rl, rows=None, what=""):
     err = np.abs(go - ro).max() if go.size else 0.0
     denom = np.linalg.norm(ro)
     rel = np.linalg.norm(go - ro) / denom if denom > 0 else np.linalg.norm(go)
+    lerr = float("nan")
+    if gl is not None:
+        live = ~np.isneginf(rl)
+        if live.any():
+            lerr = float(np.abs(gl[live] - rl[live]).max())
+    # the margins, shown by `pytest -rP`
+    print(f"parity {what}: max abs {err:.2e} (bar {MAX_ABS:.0e}), rel L2 {rel:.2e} (bar {REL_L2:.0e}), "
+          f"LSE {lerr:.2e} (bar {LSE_ABS:.0e})", flush=True)
     assert err <= MAX_ABS, f"{what}: max abs error {err:.3e}"
     assert rel <= REL_L2, f"{what}: relative L2 error {rel:.3e}"
     if gl is not None:
@@ -67,6 +75,5 @@ def assert_close(go, gl, ro, rl, rows=None, what=""):
         assert np.array_equal(np.isneginf(gl), empty), f"{what}: empty-range rows differ"
         assert np.all(go[empty] == 0), f"{what}: empty-range output not 0"
         if (~empty).any():
-            lerr = np.abs(gl[~empty] - rl[~empty]).max()
             assert lerr <= LSE_ABS, f"{what}: LSE abs error {lerr:.3e}"
     return err, rel
