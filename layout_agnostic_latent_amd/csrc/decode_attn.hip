@@ -27,8 +27,10 @@
 //  * O^T[v][head] += V^T[v][tok] . P^T[tok][head] on the same MFMA: P^T comes
 //    straight from the S^T accumulator registers (bf16), V^T from LDS with
 //    ds_read_b64_tr_b16 transposing loads.
-// The loop runs one tile behind on the output: while the matrix cores do the
-// PV products of tile j-1, the VALU computes the softmax of tile j.
+// The loop runs one tile behind on the output.  Iteration j scores tile j
+// with the exponentials of tile j-1 between its MFMAs, then updates the
+// output with tile j-1 while the VALU finds tile j's row max between the PV
+// MFMAs: the softmax runs while the matrix cores work.
 // A chunk writes normalised O and LSE (to the caller's output, or to the
 // split-KV workspace that splash_lse_merge then combines).
 #include <type_traits>
@@ -54,7 +56,7 @@ constexpr int kLdsBytes = 160 * 1024 - kPageLds * 4;
 constexpr int kMaxBuf = 4;
 constexpr float kHalfMax = 65504.0f;  // largest finite fp16 (split-KV partials are stored in fp16)
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = exp2(s - m) stays <= 256
-constexpr int kPlanStep = 22;  // PV MFMA after which the next tile's DMA plan is made (past the softmax slices)
+constexpr int kPlanStep = 22;  // PV MFMA after which the next tile's DMA plan is made (past the max slices)
 
 // LDS tile layout ("slabs"): the 16-byte chunk c of tile row r lives at
 //   (c / 8) * SLAB_B + r * 128 + ((c % 8) ^ row_swizzle(r)) * 16,
@@ -107,16 +109,21 @@ __device__ __forceinline__ float max_across_halves(float x) {
 // tile would then have to share the AGPR file with the output accumulators
 // (which fill it).  Accumulating back to back into the same registers needs
 // no wait states; the last MFMA of a chain is followed by 20 wait states so
-// that VALU instructions may read its result.
+// that VALU instructions may read its result.  The compiler takes an asm
+// statement's output as written when the statement issues, while the matrix
+// core writes it 8 passes later: a copy of the accumulator between two MFMAs
+// of a chain (a live-range split of the register allocator) would read it
+// in flight.  The accumulator is therefore pinned to fixed registers in
+// every statement of the chain, which leaves nothing to split.
 __device__ __forceinline__ void mfma_vgpr_first(floatx16& c, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "={v[2:17]}"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_vgpr(floatx16& c, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+{v[2:17]}"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_vgpr_last(floatx16& c, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3"
-               : "+v"(c)
+               : "+{v[2:17]}"(c)
                : "v"(a), "v"(b));
 }
 
@@ -502,9 +509,10 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   };
 
   // The tile loop is software-pipelined by one tile: iteration j computes the
-  // scores of tile j, then the output update of tile j-1 with the softmax of
-  // tile j interleaved between its MFMAs, so that the exponentials run while
-  // the matrix cores work instead of between the two contractions.
+  // scores of tile j with the exponentials of tile j-1 between its MFMAs,
+  // then the output update of tile j-1 with tile j's row max between those
+  // MFMAs, so that the softmax runs while the matrix cores work instead of
+  // between the two contractions.
 
   // ---- S^T = K Q^T (32 tokens x 32 heads) of tile `it` ----
   // K operands are read PF steps ahead of the MFMA that consumes them.  With
@@ -537,6 +545,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
           if ((i * C::KSW) / C::DMA_QK == s && do_dma) issue_one(dp, i);
       }
       hook(s);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (C::KSPLIT) {
       // partial tiles, lane-major: element 4q..4q+3 of lane l of wave w at
@@ -588,32 +597,13 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[r]);
     return max_across_halves(mloc) * a.scale_log2;
   };
-  // p = exp2(s * scale_log2 - m) as bf16 PV operands (tokens 16k .. 16k+15),
-  // with the exact and the rounded sums.
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  auto probs = [&](const floatx16& s, float m, bf16x8 (&p)[2], float& lsum, float& lrsum) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * k + e], a.scale_log2, -m));
-        p[k][e] = (__bf16)pf;
-        lsum += pf;
-      }
-      // sum of the rounded weights, two per v_dot2_f32_bf16
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2 pair = {p[k][2 * e], p[k][2 * e + 1]};
-        lrsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lrsum, false);
-      }
-    }
-  };
 
   // ---- O^T += V^T P^T for tile `it` ----
   // Two transposing LDS reads feed each MFMA; they run PV_PF MFMAs ahead, and
   // the first PV_PF are issued by the caller (during the score MFMAs of the
   // next tile, so that their latency is hidden).  `step(i)` emits a slice of
-  // other work (the next tile's softmax) after MFMA i; the scheduling barrier
+  // other work (the next tile's row max) after MFMA i; the scheduling barrier
   // keeps each slice between its MFMAs, where the VALU runs while the matrix
   // core is busy.
   constexpr int NM = C::NM;
@@ -648,28 +638,93 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     };
   };
 
-  // One pipelined step: scores of tile `it` are in `s`; the output update of
-  // tile it-1 (weights `pprev`) runs while tile it's softmax is computed in
-  // slices between its MFMAs.  The wave issues in order, so a slice whose
-  // instructions depend on each other would hold back the next MFMA by the
-  // whole chain's latency; every slice therefore only uses values computed
-  // in earlier slices (at least one MFMA, 32 cycles, ago):
+  // Exponentials of a finished score tile, in 19 slices: a three-stage
+  // pipeline over its 16 scores (exponent; exp2; the exact sum and the bf16
+  // pair packing with the rounded sum).  The wave issues in order, so each
+  // slice only uses values made one slice (at least one MFMA) earlier.
+  // `pin` ties a value to its slice: pure arithmetic would otherwise be sunk
+  // past the scheduling barriers to the end of the block.
+  constexpr int kExpSlices = 19;
+  auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
+  auto exp_slice = [&](int t, floatx16& sp, float m, uint32_t (&pw)[2][4], float& lsum, float& lrsum) {
+    if (t < 16) {
+      float x = __builtin_fmaf(sp[t], a.scale_log2, -m);
+      pin(x);
+      sp[t] = x;
+    }
+    if (t >= 1 && t <= 16) {
+      float x = __builtin_amdgcn_exp2f(sp[t - 1]);
+      pin(x);
+      sp[t - 1] = x;
+    }
+    if (t >= 2 && t <= 17) {
+      lsum += sp[t - 2];
+      pin(lsum);
+    }
+    if (t >= 3 && t <= 17 && ((t - 2) & 1)) {  // pack p[e-1], p[e] (e = t-2 odd)
+      const int e = t - 2;
+      const bf16x2 pair = {(__bf16)sp[e - 1], (__bf16)sp[e]};
+      uint32_t w = __builtin_bit_cast(uint32_t, pair);
+      asm volatile("" : "+v"(w));
+      pw[e >> 3][(e & 7) >> 1] = w;
+    }
+    if (t >= 4 && t <= 18 && ((t - 3) & 1)) {  // sum of the rounded pair packed one slice ago
+      const int e = t - 3;
+      lrsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e >> 3][(e & 7) >> 1]), ones, lrsum,
+                                              false);
+      pin(lrsum);
+    }
+  };
+  auto pack_probs = [](const uint32_t (&pw)[2][4], bf16x8 (&p)[2]) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const u32x4 w = {pw[k][0], pw[k][1], pw[k][2], pw[k][3]};
+      p[k] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
+  // First score MFMA whose slack takes an exponential slice (the chain's
+  // first steps carry the tile's first K reads and DMA instructions).
+  constexpr int kExpStep0 = C::KSW >= kExpSlices + 2 ? 2 : 0;
+
+  // Score phase of iteration j: the scores of tile j, with the exponentials
+  // of tile j-1 (scores `sprev`, running max m_run) in the MFMAs' slack, so
+  // that they run on the VALU while the matrix cores work.  Tile j-1's
+  // weights are first consumed by its PV products, which come after these
+  // score MFMAs.  Returns tile j's scores and tile j-1's packed weights; the
+  // sums of tile j-1's weights are added to the running sums.
+  auto qk_and_exp = [&](int it, auto with_dma, bool do_dma, const DmaPlan& dp, bf16x8 (&vring)[PV_PF],
+                        floatx16& sprev, bf16x8 (&pcur)[2]) -> floatx16 {
+    uint32_t pw[2][4];
+    float lsum = 0.0f, lrsum = 0.0f;
+    const float m = m_run;
+    auto vpf = vprefetch_hook(it - 1, vring);
+    floatx16 s = qk_tile(it, with_dma, do_dma, dp, [&](int sidx) {
+      vpf(sidx);
+      const int t = sidx - kExpStep0;
+      if (t >= 0 && t < kExpSlices) exp_slice(t, sprev, m, pw, lsum, lrsum);
+    });
+#pragma unroll
+    for (int t = C::KSW - kExpStep0; t < kExpSlices; ++t) exp_slice(t, sprev, m, pw, lsum, lrsum);
+    l_run += lsum;
+    lr_run += lrsum;
+    pack_probs(pw, pcur);
+    return s;
+  };
+
+  // PV phase of iteration j: the output update of tile j-1 (weights `pcur`),
+  // with tile j's row max and the new running max in slices between its
+  // MFMAs; every slice only uses values made in earlier slices:
   //   slices 0-6: the row max (a max3 tree, then the other half's max),
-  //   7-9:        scaled max and the new running max,
-  //   10-28:      a three-stage pipeline over the 16 scores: exponent,
-  //               exp2, then the sum and the bf16 pair packing.
-  auto pv_and_softmax = [&](int it, floatx16& s, bf16x8 (&pprev)[2], bf16x8 (&vring)[PV_PF], auto with_dma,
-                            const DmaPlan& dp, auto&& extra) {
+  //   7-9:        scaled max and the new running max.
+  // After the products, the output and the running sums are rescaled to the
+  // new max if it moved (lazily: only when it grew by more than 2^8).
+  auto pv_and_max = [&](int it, floatx16& s, const bf16x8 (&pcur)[2], bf16x8 (&vring)[PV_PF], auto with_dma,
+                        const DmaPlan& dp, auto&& extra) {
     mask_tile(s, it);
     float mx[4];
     float m_new = m_run;
     const float thr = m_run + kRescaleThreshold;
     bool need = false;
-    uint32_t pw[2][4];
-    float lsum = 0.0f, lrsum = 0.0f;
-    // `pin` ties a value to its slice: pure arithmetic would otherwise be
-    // sunk past the scheduling barriers to the end of the block.
-    auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
     auto max3 = [](float x, float y, float z) {
       float r;
       asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
@@ -713,40 +768,11 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
       } else if (i == 9) {
         m_new = need ? mx[0] : m_run;
         pin(m_new);
-      } else if (i < 10 + 19) {
-        const int t = i - 10;
-        if (t < 16) {
-          float x = __builtin_fmaf(s[t], a.scale_log2, -m_new);
-          pin(x);
-          s[t] = x;
-        }
-        if (t >= 1 && t <= 16) {
-          float x = __builtin_amdgcn_exp2f(s[t - 1]);
-          pin(x);
-          s[t - 1] = x;
-        }
-        if (t >= 2 && t <= 17) {
-          lsum += s[t - 2];
-          pin(lsum);
-        }
-        if (t >= 3 && t <= 17 && ((t - 2) & 1)) {  // pack p[e-1], p[e] (e = t-2 odd)
-          const int e = t - 2;
-          const bf16x2 pair = {(__bf16)s[e - 1], (__bf16)s[e]};
-          uint32_t w = __builtin_bit_cast(uint32_t, pair);
-          asm volatile("" : "+v"(w));
-          pw[e >> 3][(e & 7) >> 1] = w;
-        }
-        if (t >= 4 && t <= 18 && ((t - 3) & 1)) {  // sum of the rounded pair packed one slice ago
-          const int e = t - 3;
-          lrsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e >> 3][(e & 7) >> 1]), ones, lrsum,
-                                                  false);
-          pin(lrsum);
-        }
       }
     };
-    pv_tile(it - 1, pprev, vring, step);
+    pv_tile(it - 1, pcur, vring, step);
     // slices beyond the MFMA count (variants with fewer V blocks)
-    constexpr int kSteps = 10 + 19 > kPlanStep + 1 ? 10 + 19 : kPlanStep + 1;
+    constexpr int kSteps = 10 > kPlanStep + 1 ? 10 : kPlanStep + 1;
 #pragma unroll
     for (int i = C::NM; i < kSteps; ++i) step(i);
     const bool any_need = __any(need);
@@ -767,13 +793,6 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
         }
     }
     m_run = m_new;
-    l_run += lsum;
-    lr_run += lrsum;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const u32x4 w = {pw[k][0], pw[k][1], pw[k][2], pw[k][3]};
-      pprev[k] = __builtin_bit_cast(bf16x8, w);
-    }
   };
 
   const std::integral_constant<bool, true> kDma;
@@ -831,10 +850,11 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
       for (int k = 0; k < C::DMA_W; ++k) issue_one(d, k);
     }
 
-  // Iteration 0: scores and softmax of tile 0 (the output is still zero, so
-  // the running max is simply set).  Tile 2's DMA goes into its free slot.
-  bf16x8 pprev[2];
-  DmaPlan dp;  // DMA of the tile two ahead of the one being scored
+  // Iteration 0: scores and row max of tile 0 (the output is still zero, so
+  // the running max is simply set; its exponentials run during the next
+  // scores).  Tile 2's DMA goes into its free slot.
+  floatx16 sprev;  // masked scores of the previous tile, awaiting their exponentials
+  DmaPlan dp;      // DMA of the tile two ahead of the one being scored
   {
     if (ntiles > 1) wait_vmcnt<C::DMA_W>();
     else wait_vmcnt<0>();
@@ -851,27 +871,30 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     }
     mask_tile(s, 0);
     m_run = tile_max(s);
-    probs(s, m_run, pprev, l_run, lr_run);
+    sprev = s;
     if (3 < ntiles) dp = dma_plan(t_begin + 3, 3 % C::NBUF, pages_of(t_begin + 3));
   }
 
   // Main loop, iteration j: wait for tile j and barrier (every wave is done
   // with tile j-2, whose slot takes tile j+2); scores of tile j with the DMA
-  // of tile j+2 interleaved; output update of tile j-1 with tile j's softmax,
-  // and, in the PV MFMAs' slack after the softmax, the page lookups and DMA
-  // plan of tile j+3 (scalar work, off the path into the next scores).
+  // of tile j+2 and the exponentials of tile j-1 interleaved; output update
+  // of tile j-1 with tile j's row max, and, in the PV MFMAs' slack after the
+  // max, the page lookups and DMA plan of tile j+3 (scalar work, off the path
+  // into the next scores).
   // One younger tile (j+1) stays in flight across the wait.
   int it = 1;
   for (; it + 2 < ntiles; ++it) {
     wait_vmcnt<C::DMA_W>();
     __syncthreads();
     bf16x8 vring[PV_PF];
-    floatx16 s = qk_tile(it, kDma, true, dp, vprefetch_hook(it - 1, vring));
+    bf16x8 pcur[2];
+    floatx16 s = qk_and_exp(it, kDma, true, dp, vring, sprev, pcur);
     DmaPlan dp_next = dp;
     const int tn = t_begin + it + 3;
-    pv_and_softmax(it, s, pprev, vring, kDma, dp, [&](int i) {
+    pv_and_max(it, s, pcur, vring, kDma, dp, [&](int i) {
       if (i == kPlanStep && tn < t_end) dp_next = dma_plan(tn, (it + 3) % C::NBUF, pages_of(tn));
     });
+    sprev = s;
     dp = dp_next;
   }
   const DmaPlan none{nullptr, nullptr, 0u, 0, 0, nullptr, 0u};
@@ -880,15 +903,25 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     else wait_vmcnt<0>();
     __syncthreads();
     bf16x8 vring[PV_PF];
-    floatx16 s = qk_tile(it, kNoDma, false, none, vprefetch_hook(it - 1, vring));
-    pv_and_softmax(it, s, pprev, vring, kNoDma, none, [](int) {});
+    bf16x8 pcur[2];
+    floatx16 s = qk_and_exp(it, kNoDma, false, none, vring, sprev, pcur);
+    pv_and_max(it, s, pcur, vring, kNoDma, none, [](int) {});
+    sprev = s;
   }
-  // Output update of the last tile.
+  // Weights and output update of the last tile.
   {
     bf16x8 vring[PV_PF];
 #pragma unroll
     for (int i = 0; i < PV_PF; ++i) vring[i] = vread(ntiles - 1, i);
-    pv_tile(ntiles - 1, pprev, vring, [](int) {});
+    uint32_t pw[2][4];
+    float lsum = 0.0f, lrsum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kExpSlices; ++t) exp_slice(t, sprev, m_run, pw, lsum, lrsum);
+    l_run += lsum;
+    lr_run += lrsum;
+    bf16x8 plast[2];
+    pack_probs(pw, plast);
+    pv_tile(ntiles - 1, plast, vring, [](int) {});
   }
   // let the last PV MFMAs retire before the epilogue reads the accumulators
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
