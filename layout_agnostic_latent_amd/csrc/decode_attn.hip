@@ -73,8 +73,10 @@ __device__ __forceinline__ uint32_t row_swizzle(uint32_t row) {
 // (SGPRs) plus a per-lane 32-bit offset; lane i's 16 bytes land at
 // lds_addr + 16*i.  Issued from inline asm so that the compiler does not add
 // a vmcnt(0) before every LDS read; completion is tracked by wait_vmcnt().
+// Every KV byte is read once per call, so the load is non-temporal (nt):
+// the stream does not displace reusable lines from the caches.
 __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)),
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)),
                "v"(voff), "s"(sbase)
                : "memory");
 }
