@@ -188,6 +188,28 @@ typedef struct splash_profile {
 int splash_profile_start(void);
 int splash_profile_stop(splash_profile* out);
 
+/*
+ * Peaks of the current GPU as measured (roofline context for the kernels
+ * above; no part of the attention path):
+ *  - mfma_bf16_tflops: dense v_mfma_f32_32x32x16_bf16 rate with one wave per
+ *    SIMD on every CU, best of three ~2 ms runs;
+ *  - mfma_clock_ghz: the shader clock during that run (s_memtime cycles
+ *    over the 100 MHz s_memrealtime clock, averaged over workgroups);
+ *  - hbm_read_gbps: streaming read rate over the caller's device buffer
+ *    `buf` of `bytes` (>= 1 MiB, 16-byte aligned; use >= 1 GiB so that the
+ *    256 MiB Infinity Cache does not serve it), best of three.
+ * Synchronises `stream`.  Returns SPLASH_OK, SPLASH_EINVAL (bad arguments)
+ * or SPLASH_EHIP.  Results live in a small per-device array the library
+ * owns; concurrent calls on one device race on it.
+ */
+typedef struct splash_peaks {
+  double mfma_bf16_tflops;
+  double mfma_clock_ghz;
+  double hbm_read_gbps;
+} splash_peaks;
+
+int splash_measure_peaks(const void* buf, int64_t bytes, splash_peaks* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["LIB_PATH", "SplashError", "lib", "decode_attn", "decode_plan", "lse_merge", "kv_repack",
-           "device_errors", "release_workspace", "profile_start", "profile_stop", "DEVERR_BAD_PAGE",
+           "device_errors", "release_workspace", "profile_start", "profile_stop", "measure_peaks", "DEVERR_BAD_PAGE",
            "DEVERR_REPACK_PAIR", "DEVERR_PARTIAL_RANGE"]
 
 # The in-tree build; SPLASH_LIB may name another build of the same library.
@@ -45,6 +45,11 @@ class Profile(ctypes.Structure):
     _fields_ = [("decode_launches", ctypes.c_int32), ("merge_launches", ctypes.c_int32),
                 ("repack_launches", ctypes.c_int32), ("decode_ms", ctypes.c_double),
                 ("merge_ms", ctypes.c_double), ("repack_ms", ctypes.c_double)]
+
+
+class Peaks(ctypes.Structure):
+    _fields_ = [("mfma_bf16_tflops", ctypes.c_double), ("mfma_clock_ghz", ctypes.c_double),
+                ("hbm_read_gbps", ctypes.c_double)]
 
 
 _lib = None
@@ -77,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.splash_profile_start.restype = ctypes.c_int
         L.splash_profile_stop.argtypes = [ctypes.POINTER(Profile)]
         L.splash_profile_stop.restype = ctypes.c_int
+        L.splash_measure_peaks.argtypes = [vp, i64, ctypes.POINTER(Peaks), vp]
+        L.splash_measure_peaks.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -220,3 +227,15 @@ def profile_stop() -> dict:
     p = Profile()
     _check(lib().splash_profile_stop(ctypes.byref(p)))
     return {f: getattr(p, f) for f, _ in Profile._fields_}
+
+
+def measure_peaks(buf, stream=None) -> dict:
+    """splash_measure_peaks over the device tensor `buf` (>= 1 MiB; use >= 1 GiB): measured bf16 MFMA
+    TFLOP/s, the shader clock during it (GHz), and the streaming HBM read rate (GB/s)."""
+    import torch
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    p = Peaks()
+    _check(lib().splash_measure_peaks(_ptr(buf), buf.numel() * buf.element_size(), ctypes.byref(p), _stream(stream)))
+    return {"mfma_bf16_tflops": p.mfma_bf16_tflops, "mfma_clock_ghz": p.mfma_clock_ghz,
+            "hbm_read_gbps": p.hbm_read_gbps}

