@@ -161,8 +161,40 @@ __device__ int4 plan_item(const DecodeArgs& a, int32_t* scratch) {
   long long total = 0;
   for (int w = 0; w < NWV; ++w) total += red[w];
   const long long full_cap = (long long)a.plan_target * a.plan_max_chunk;
-  const int chunk = total >= full_cap ? a.plan_max_chunk
-                                      : max(a.plan_min_chunk, ((int)total + a.plan_target - 1) / a.plan_target);
+  int chunk = total >= full_cap ? a.plan_max_chunk
+                                : max(a.plan_min_chunk, ((int)total + a.plan_target - 1) / a.plan_target);
+  if (chunk < a.plan_max_chunk) {
+    // Items with chunk length c: sum over requests of ceil(tiles / c), a
+    // block-wide count (every thread gets the same value).
+    int* cnt = scratch + 2 * NWV + 8;  // [NWV], clear of red[]
+    auto items_at = [&](int c) -> int {
+      int m = 0;
+      for (int k = 0; k < per; ++k) {
+        const int r = tid * per + k;
+        if (r < a.num_reqs) m += (tiles(r) + c - 1) / c;
+      }
+      for (int d = 32; d >= 1; d >>= 1) m += __shfl_xor(m, d, 64);
+      if (lane == 0) cnt[wave] = m;
+      __syncthreads();
+      int n = 0;
+      for (int w = 0; w < NWV; ++w) n += cnt[w];
+      __syncthreads();
+      return n;
+    };
+    // A ragged batch's remainder chunks can overflow one round of plan_target
+    // workgroups; the items past it then start only when earlier ones end,
+    // which can double the critical path.  Take the shortest chunk that fits
+    // one round instead, if any chunk up to the maximum does.
+    if (items_at(chunk) > a.plan_target && items_at(a.plan_max_chunk) <= a.plan_target) {
+      int lo = chunk, hi = a.plan_max_chunk;  // items_at(lo) > target >= items_at(hi)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (items_at(mid) <= a.plan_target) hi = mid;
+        else lo = mid;
+      }
+      chunk = hi;
+    }
+  }
   int nf = 0, nr = 0;
   for (int k = 0; k < per; ++k) {
     const int r = tid * per + k;
