@@ -300,6 +300,9 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
 }
 
 }  // namespace
+
+int report_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
 }  // namespace splash
 
 using namespace splash;

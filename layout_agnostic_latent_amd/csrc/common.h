@@ -67,6 +67,10 @@ struct DecodeVariant {
   int d_qk, d_v, wh, wv;
 };
 
+// Records `msg` as the thread's last error (splash_last_error) and returns
+// `code`; for entry points defined outside api.hip.
+int report_error(int code, const char* msg);
+
 // Each launcher takes two optional events that, when non-null, record the
 // start and end of the kernel itself (hipExtLaunchKernelGGL), for profiling.
 hipError_t launch_decode(const DecodeVariant& v, dim3 grid, const DecodeArgs& a, hipStream_t stream,

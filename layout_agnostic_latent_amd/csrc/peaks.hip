@@ -81,14 +81,18 @@ float elapsed_ms(hipEvent_t a, hipEvent_t b) {
 using namespace splash;
 
 extern "C" int splash_measure_peaks(const void* buf, int64_t bytes, splash_peaks* out, hipStream_t stream) {
-  if (!out) return SPLASH_EINVAL;
+  if (!out) return report_error(SPLASH_EINVAL, "splash_measure_peaks: out is NULL");
   if (!buf || bytes < (int64_t)1 << 20 || (((uintptr_t)buf) & 15))
-    return SPLASH_EINVAL;
+    return report_error(SPLASH_EINVAL, "splash_measure_peaks: buf must be a 16-byte aligned device buffer of >= 1 MiB");
   *out = splash_peaks{};
   uint64_t* sink = nullptr;
-  if (hipGetSymbolAddress((void**)&sink, HIP_SYMBOL(g_splash_peak_sink)) != hipSuccess) return SPLASH_EHIP;
+  if (hipGetSymbolAddress((void**)&sink, HIP_SYMBOL(g_splash_peak_sink)) != hipSuccess)
+    return report_error(SPLASH_EHIP, "splash_measure_peaks: hipGetSymbolAddress failed");
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return SPLASH_EHIP;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) hipEventDestroy(e0);
+    return report_error(SPLASH_EHIP, "splash_measure_peaks: hipEventCreate failed");
+  }
   int rc = SPLASH_OK;
   // MFMA: one workgroup per CU, 4 waves; ~2.4 ms of products at 2.4 GHz.
   constexpr int kBlocks = 256;
@@ -135,5 +139,6 @@ extern "C" int splash_measure_peaks(const void* buf, int64_t bytes, splash_peaks
   }
   hipEventDestroy(e0);
   hipEventDestroy(e1);
+  if (rc != SPLASH_OK) return report_error(rc, "splash_measure_peaks: a launch or synchronisation failed");
   return rc;
 }

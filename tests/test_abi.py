@@ -151,3 +151,13 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(root, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_measure_peaks_rejects_bad_arguments_without_a_gpu(splash):
+    L = splash.lib()
+    p = sp.Peaks()
+    assert L.splash_measure_peaks(None, 1 << 30, ctypes.byref(p), None) == sp.EINVAL
+    assert b"measure_peaks" in L.splash_last_error()
+    assert L.splash_measure_peaks(0x1000, 1000, ctypes.byref(p), None) == sp.EINVAL   # under 1 MiB
+    assert L.splash_measure_peaks(0x1001, 1 << 30, ctypes.byref(p), None) == sp.EINVAL  # misaligned
+    assert L.splash_measure_peaks(0x1000, 1 << 30, None, None) == sp.EINVAL

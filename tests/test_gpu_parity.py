@@ -486,3 +486,21 @@ def test_repack_unaligned_page_bytes():
     want, _, _ = oracle.kv_repack(src.cpu().numpy(), st.cpu().numpy(), np.zeros((7, 3, 5), np.int16),
                                   dt.cpu().numpy())
     assert np.array_equal(dst.cpu().numpy(), want)
+
+
+# ---------------------------------------------------------------------------
+# measured peaks (roofline context; no part of the path)
+# ---------------------------------------------------------------------------
+def test_measure_peaks_is_plausible():
+    buf = torch.ones(256 << 20, dtype=torch.uint8, device=DEV)
+    _print("case measure_peaks over 256 MiB")
+    pk = sp.measure_peaks(buf)
+    _print(f"  {pk}")
+    # dense bf16 MFMA: below the 2.5 PFLOP/s published peak, far above a
+    # broken loop; the shader clock within the part's range; the read rate
+    # below the 256 MiB Infinity Cache's bandwidth and above a trickle
+    assert 500.0 < pk["mfma_bf16_tflops"] < 2600.0
+    assert 0.5 < pk["mfma_clock_ghz"] < 2.6
+    assert 500.0 < pk["hbm_read_gbps"] < 20000.0
+    with pytest.raises(sp.SplashError):
+        sp.measure_peaks(buf[:1000])   # under 1 MiB
