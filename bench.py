@@ -446,32 +446,48 @@ def measured_traffic(workload, kernel_prefix):
 
 
 def cpu_baseline(case, budget_s):
-    """The float64 oracle on the host cores, on requests of the same batch, for about budget_s seconds."""
+    """The float64 oracle on the host cores, on requests of the same batch, for about budget_s seconds; then
+    the same with BLAS limited to one thread, for a third of that."""
     import numpy as np
     import oracle
     cores = len(os.sched_getaffinity(0))
+    blas = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = max([p.get("num_threads", 1) for p in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:  # pragma: no cover
-        threads = cores
-    done_tokens = 0
-    reqs = 0
-    t0 = time.perf_counter()
-    b = 0
-    while True:
-        oracle.decode_attn(case.q, case.kv_pages, case.block_table, case.seq_lens, case.head_lo, case.head_hi,
-                           case.tok_lo, case.tok_hi, case.d_v, case.page_size, case.scale, reqs=[b])
-        lo = max(case.tok_lo, 0)
-        done_tokens += max(0, min(case.tok_hi, int(case.seq_lens[b])) - lo)
-        reqs += 1
-        b = (b + 1) % case.num_reqs
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+        threads, threadpool_limits = cores, None
+
+    def run(seconds):
+        done_tokens = 0
+        reqs = 0
+        t0 = time.perf_counter()
+        b = 0
+        while True:
+            oracle.decode_attn(case.q, case.kv_pages, case.block_table, case.seq_lens, case.head_lo, case.head_hi,
+                               case.tok_lo, case.tok_hi, case.d_v, case.page_size, case.scale, reqs=[b])
+            lo = max(case.tok_lo, 0)
+            done_tokens += max(0, min(case.tok_hi, int(case.seq_lens[b])) - lo)
+            reqs += 1
+            b = (b + 1) % case.num_reqs
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return done_tokens, reqs, el
+
+    done_tokens, reqs, el = run(budget_s)
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            t1, _, e1 = run(budget_s / 3.0)
+        one = round(t1 / e1, 1)
     return {"value": round(done_tokens / el, 1), "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
+            "value_1_thread": one, "blas": blas,
             "sample": f"{reqs} requests of the same batch (float64 numpy, {done_tokens} KV tokens, {el:.1f} s; "
-                      f"{cores} cores in the affinity mask)"}
+                      f"{cores} cores in the affinity mask); value_1_thread: the same loop with BLAS limited to one "
+                      f"thread for {budget_s / 3.0:.1f} s"}
 
 
 if __name__ == "__main__":
