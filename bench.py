@@ -166,6 +166,7 @@ def main():
                                              case.max_pages_per_req, case.num_pages, case.scale, case.head_lo,
                                              case.head_hi, case.tok_lo, case.tok_hi, splits)[0] > 1 else 0
     merge_us = 1e3 * prof["merge_ms"] / max(1, prof["merge_launches"])
+    lse_merge_us = 1e3 * prof["lse_merge_ms"] / max(1, prof["lse_merge_launches"])
     repack_us = 1e3 * prof["repack_ms"] / max(1, prof["repack_launches"])
 
     # algorithmic bytes and flops of one decode-attention call
@@ -194,8 +195,8 @@ def main():
         parts["repack_hbm_frac"] = round(2 * moved / (repack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     if mrg is not None:
         mb = mrg["P"].numel() * 4 + mrg["L"].numel() * 4 + mrg["out"].numel() * 4 + mrg["lse"].numel() * 4
-        parts["lse_merge_us"] = round(merge_us, 2)
-        parts["lse_merge_TBps"] = round(mb / (merge_us * 1e-6) / 1e12, 3)
+        parts["lse_merge_us"] = round(lse_merge_us, 2)
+        parts["lse_merge_TBps"] = round(mb / (lse_merge_us * 1e-6) / 1e12, 3)
 
     traffic = measured_traffic(args.workload, "decode_attn_kernel")
 

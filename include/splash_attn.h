@@ -177,12 +177,14 @@ int splash_decode_plan(const splash_desc* desc, int32_t head_lo, int32_t head_hi
  * records per launch and is not thread-safe across concurrent callers.
  */
 typedef struct splash_profile {
-  int32_t decode_launches;  /* decode-attention kernels (one per splash_decode_attn) */
-  int32_t merge_launches;   /* merge kernels (split-KV merges and splash_lse_merge) */
-  int32_t repack_launches;  /* splash_kv_repack kernels */
-  double decode_ms;         /* summed kernel durations, milliseconds */
+  int32_t decode_launches;     /* decode-attention kernels (one per splash_decode_attn) */
+  int32_t merge_launches;      /* split-KV merge kernels inside splash_decode_attn */
+  int32_t repack_launches;     /* splash_kv_repack kernels */
+  double decode_ms;            /* summed kernel durations, milliseconds */
   double merge_ms;
   double repack_ms;
+  int32_t lse_merge_launches;  /* splash_lse_merge kernels */
+  double lse_merge_ms;
 } splash_profile;
 
 int splash_profile_start(void);

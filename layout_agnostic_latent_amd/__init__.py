@@ -44,7 +44,8 @@ class Desc(ctypes.Structure):
 class Profile(ctypes.Structure):
     _fields_ = [("decode_launches", ctypes.c_int32), ("merge_launches", ctypes.c_int32),
                 ("repack_launches", ctypes.c_int32), ("decode_ms", ctypes.c_double),
-                ("merge_ms", ctypes.c_double), ("repack_ms", ctypes.c_double)]
+                ("merge_ms", ctypes.c_double), ("repack_ms", ctypes.c_double),
+                ("lse_merge_launches", ctypes.c_int32), ("lse_merge_ms", ctypes.c_double)]
 
 
 class Peaks(ctypes.Structure):

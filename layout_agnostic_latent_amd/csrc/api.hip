@@ -40,7 +40,7 @@ int fail_hip(hipError_t e, const char* what) {
 }
 
 // Launch profiling: events bracketing each kernel while enabled.
-enum LaunchKind { kDecode = 0, kMerge = 1, kRepack = 2 };
+enum LaunchKind { kDecode = 0, kMerge = 1, kRepack = 2, kLseMerge = 3 };
 struct TimedLaunch {
   int kind;
   hipEvent_t start, stop;
@@ -454,7 +454,7 @@ int splash_lse_merge(const float* partials, const float* lses, int32_t n_parts, 
   hipError_t e;
   {
     std::lock_guard<std::mutex> lock(g_mu);
-    e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
+    e = timed(kLseMerge, [&](hipEvent_t e0, hipEvent_t e1) {
       return launch_lse_merge(partials, lses, n_parts, rows, d_v, out, lse_out, stream, e0, e1);
     });
   }
@@ -541,6 +541,7 @@ int splash_profile_stop(splash_profile* out) {
     if (t.kind == kDecode) { p.decode_launches++; p.decode_ms += ms; }
     if (t.kind == kMerge) { p.merge_launches++; p.merge_ms += ms; }
     if (t.kind == kRepack) { p.repack_launches++; p.repack_ms += ms; }
+    if (t.kind == kLseMerge) { p.lse_merge_launches++; p.lse_merge_ms += ms; }
     g_event_pool.push_back(t.start);
     g_event_pool.push_back(t.stop);
   }

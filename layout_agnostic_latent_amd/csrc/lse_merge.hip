@@ -134,17 +134,40 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(const float* _
   if (lse_out && tid == 0) lse_out[row] = lse;
 }
 
-// Split-KV merge: one wave per output row, each lane 8 columns.  The LSEs
-// and fp16 partial rows of up to kSplitBatch parts are loaded in one round
-// (no address depends on a loaded value: a part with LSE -inf, whose row the
-// decode kernel never wrote, is read but given no weight), then combined,
-// with an online rescale of the sums when a row has more parts.  No LDS and
-// no barrier: the row's cost is one round trip to memory.
+// Row-wave merge: one wave per output row, each lane 8 columns (d_v <= 512,
+// a multiple of 8).  The LSEs and partial rows of up to kSplitBatch parts are
+// loaded in one round (no address depends on a loaded value: a part with LSE
+// -inf, whose row may never have been written, is read but given no weight
+// by a select, so garbage in it cannot reach the sums), then combined, with
+// an online rescale of the sums when a row has more parts.  No LDS and no
+// barrier: the row's cost is one round trip to memory.  T is the partial
+// element type: fp16 (split-KV partials) or fp32 (the caller's partials).
 constexpr int kSplitBatch = 16;
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 
-template <typename Parts>
-__global__ void __launch_bounds__(256) split_merge_kernel(const _Float16* __restrict__ P, const float* __restrict__ L,
+// 8 consecutive partial values of one lane.
+template <typename T>
+struct Row8;
+template <>
+struct Row8<_Float16> {
+  halfx8 v;
+  __device__ void load(const _Float16* p) { v = *(const halfx8*)p; }
+  __device__ void zero() { v = halfx8{}; }
+  __device__ float get(int k) const { return (float)v[k]; }
+};
+template <>
+struct Row8<float> {
+  floatx4 a, b;
+  __device__ void load(const float* p) {
+    a = ((const floatx4*)p)[0];
+    b = ((const floatx4*)p)[1];
+  }
+  __device__ void zero() { a = b = floatx4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ float get(int k) const { return k < 4 ? a[k] : b[k - 4]; }
+};
+
+template <typename T, typename Parts>
+__global__ void __launch_bounds__(256) split_merge_kernel(const T* __restrict__ P, const float* __restrict__ L,
                                                           Parts parts, int32_t rows, int32_t d_v,
                                                           float* __restrict__ out, float* __restrict__ lse_out) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -159,13 +182,14 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const _Float16* __rest
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < n; p0 += kSplitBatch) {
     float l[kSplitBatch];
-    halfx8 v[kSplitBatch];
+    Row8<T> v[kSplitBatch];
 #pragma unroll
     for (int u = 0; u < kSplitBatch; ++u) {
       const bool live = p0 + u < n;
       const int64_t pi = live ? rp.index(p0 + u) : 0;
       l[u] = live ? L[pi] : -INFINITY;
-      v[u] = (live && active) ? *(const halfx8*)(P + pi * d_v + c) : halfx8{};
+      if (live && active) v[u].load(P + pi * d_v + c);
+      else v[u].zero();
     }
     float mb = M;
 #pragma unroll
@@ -181,7 +205,7 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const _Float16* __rest
         const float w = __expf(l[u] - mb);
         S += w;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] += w * (float)v[u][k];
+        for (int k = 0; k < 8; ++k) acc[k] += w * v[u].get(k);
       }
     }
     M = mb;
@@ -209,8 +233,8 @@ hipError_t launch_split_merge(const uint16_t* partials, const float* lses, int32
                               int32_t d_v, float* out, float* lse_out, hipStream_t stream, hipEvent_t e0,
                               hipEvent_t e1) {
   if (rows == 0) return hipSuccess;
-  hipExtLaunchKernelGGL(split_merge_kernel<UniformParts>, dim3((rows + 3) / 4), dim3(256), 0, stream, e0, e1, 0,
-                        (const _Float16*)partials, lses, UniformParts{n_parts, rows}, rows, d_v, out, lse_out);
+  hipExtLaunchKernelGGL((split_merge_kernel<_Float16, UniformParts>), dim3((rows + 3) / 4), dim3(256), 0, stream, e0,
+                        e1, 0, (const _Float16*)partials, lses, UniformParts{n_parts, rows}, rows, d_v, out, lse_out);
   return hipGetLastError();
 }
 
@@ -218,8 +242,8 @@ hipError_t launch_split_merge_segmented(const uint16_t* partials, const float* l
                                         int32_t rows, int32_t hs, int32_t d_v, float* out, float* lse_out,
                                         hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   if (rows == 0) return hipSuccess;
-  hipExtLaunchKernelGGL(split_merge_kernel<ListedParts>, dim3((rows + 3) / 4), dim3(256), 0, stream, e0, e1, 0,
-                        (const _Float16*)partials, lses, ListedParts{req_info, hs}, rows, d_v, out, lse_out);
+  hipExtLaunchKernelGGL((split_merge_kernel<_Float16, ListedParts>), dim3((rows + 3) / 4), dim3(256), 0, stream, e0,
+                        e1, 0, (const _Float16*)partials, lses, ListedParts{req_info, hs}, rows, d_v, out, lse_out);
   return hipGetLastError();
 }
 
@@ -227,6 +251,12 @@ hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_
                             int32_t d_v, float* out, float* lse_out, hipStream_t stream, hipEvent_t e0,
                             hipEvent_t e1) {
   if (rows == 0) return hipSuccess;
+  if (d_v % 8 == 0 && d_v <= 512) {
+    // one wave per row, every load of a row in one round
+    hipExtLaunchKernelGGL((split_merge_kernel<float, UniformParts>), dim3((rows + 3) / 4), dim3(256), 0, stream, e0,
+                          e1, 0, partials, lses, UniformParts{n_parts, rows}, rows, d_v, out, lse_out);
+    return hipGetLastError();
+  }
   hipExtLaunchKernelGGL(lse_merge_kernel<UniformParts>, dim3(rows), dim3(kMergeThreads), 0, stream, e0, e1, 0,
                         partials, lses, UniformParts{n_parts, rows}, d_v, out, lse_out);
   return hipGetLastError();
