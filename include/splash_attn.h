@@ -117,12 +117,13 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
  *   M = max_p lses[p][r] over finite entries
  *   lse_out[r] = M + log(sum_p exp(lses[p][r] - M))
  *   out[r][:]  = sum_p exp(lses[p][r] - lse_out[r]) * partials[p][r][:]
- * Parts with lse = -inf count for nothing (their partials are not read); a
- * row with no live part gets out = 0, lse_out = -inf.
+ * Parts with lse = -inf count for nothing: whatever their partial rows hold
+ * (NaN included) does not reach the result, though the whole partials buffer
+ * may be read; a row with no live part gets out = 0, lse_out = -inf.
  *   partials fp32 [n_parts][rows][d_v], lses fp32 [n_parts][rows]
  *   out fp32 [rows][d_v], lse_out fp32 [rows] or NULL
- * Errors: SPLASH_EINVAL for null pointers, n_parts < 1, rows < 0, d_v < 1 or
- * d_v not a multiple of 4.
+ * Errors: SPLASH_EINVAL for null pointers, n_parts < 1, rows < 0, d_v < 1,
+ * d_v not a multiple of 4, or partials / out not 16-byte aligned.
  */
 int splash_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows,
                      int32_t d_v, float* out, float* lse_out, hipStream_t stream);

@@ -43,7 +43,13 @@ def kernel_source_hash() -> str:
 
 
 def short(name: str) -> str:
-    for key in ("decode_attn_kernel", "lse_merge_kernel", "split_merge_kernel", "kv_repack_kernel"):
+    # the row-wave merge serves the split-KV partials (fp16, inside
+    # splash_decode_attn) and splash_lse_merge (fp32): keep them apart
+    if "split_merge_kernel" in name:
+        if "<float" in name or "split_merge_kernelIf" in name:
+            return "split_merge_kernel<fp32> (splash_lse_merge)"
+        return "split_merge_kernel<fp16> (split-KV merge)"
+    for key in ("decode_attn_kernel", "lse_merge_kernel", "kv_repack_kernel", "mfma_peak_kernel", "read_peak_kernel"):
         if key in name:
             i = name.find("<")
             j = name.find(">", i)

@@ -424,19 +424,20 @@ def test_partial_range_is_clamped_and_flagged():
     assert np.all(np.isfinite(gs)) and np.abs(gs).max() <= 65504.0
 
 
-def test_merge_edges():
-    rows, d_v = 5, 512
+@pytest.mark.parametrize("d_v", [512, 516])  # one wave per row; the workgroup form (d_v not a multiple of 8)
+def test_merge_edges(d_v):
+    rows = 5
     P = torch.randn((3, rows, d_v), dtype=torch.float32, device=DEV)
     L = torch.tensor([[0.0, -math.inf, 1.0, -math.inf, 2.0],
                       [1.0, -math.inf, -math.inf, -math.inf, 2.0],
                       [-math.inf, -math.inf, 0.5, 3.0, 2.0]], dtype=torch.float32, device=DEV)
-    P[0, 1] = float("nan")  # a part with LSE -inf is never read
+    P[0, 1] = float("nan")  # a part with LSE -inf contributes nothing, whatever its row holds
     out = torch.empty((rows, d_v), dtype=torch.float32, device=DEV)
     lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
     sp.lse_merge(P, L, out, lse)
     torch.cuda.synchronize()
     ro, rl = oracle.lse_merge(P.cpu().numpy(), L.cpu().numpy())
-    assert_close(out.cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl, what="merge edges")
+    assert_close(out.cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl, what=f"merge edges d_v={d_v}")
     o1 = torch.empty_like(out)
     sp.lse_merge(P[:1].contiguous(), L[:1].contiguous(), o1)
     torch.cuda.synchronize()
@@ -444,10 +445,12 @@ def test_merge_edges():
     assert torch.allclose(o1[live], P[0][live], atol=1e-6, rtol=0)
 
 
-@pytest.mark.parametrize("n_parts,rows,d_v", [(300, 7, 512), (3000, 3, 64), (17, 33, 512), (1, 4, 64)])
+@pytest.mark.parametrize("n_parts,rows,d_v", [(300, 7, 512), (3000, 3, 64), (17, 33, 512), (1, 4, 64),
+                                              (3000, 3, 12), (300, 7, 1028)])
 def test_merge_many_parts(n_parts, rows, d_v):
-    """Part counts past the LDS weight store (2,048) and narrow rows (many part
-    groups per row); some parts empty."""
+    """Part counts past one batch (16) and past the workgroup form's LDS
+    weight store (2,048); widths that take the workgroup form (d_v not a
+    multiple of 8, or above 512); some parts empty."""
     g = torch.Generator(device="cpu").manual_seed(n_parts)
     P = torch.randn((n_parts, rows, d_v), generator=g, dtype=torch.float32).to(DEV)
     L = (torch.rand((n_parts, rows), generator=g, dtype=torch.float32) * 20 - 10).to(DEV)
