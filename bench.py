@@ -16,6 +16,10 @@ that KV reads come from HBM.
 Prints ONE JSON line: KV tokens/s over the step, the decode kernel's HBM
 roofline (algorithmic bytes / its measured duration), and the CPU oracle's
 throughput on a bounded sample of the same workload.
+
+Pages cited: the weekinpapers page is "SPLASH: Switching Parallel Layouts of Attention with
+Seamless Handoff for LLM Serving" (weekinpapers.com); the thelatestinai page is that paper's
+summary with its appendix tables (thelatestinai.com).
 """
 import argparse
 import json
@@ -84,8 +88,9 @@ def build_workload(name):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported "
-              "(this build runs on a single MI355X).", file=sys.stderr)
+        print(f"bench.py measures one GPU's share of a layout; --gpus {args.gpus} is not supported: "
+              "the library runs on a single MI355X (the multi-GPU exchange of a layout is not implemented).",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -3,6 +3,11 @@
  * KV head, the merge of partial results, and the KV-page repack, for AMD
  * Instinct MI355X (gfx950).
  *
+ * Pages cited: the weekinpapers page is "SPLASH: Switching Parallel Layouts of
+ * Attention with Seamless Handoff for LLM Serving" (weekinpapers.com); the
+ * thelatestinai page is that paper's summary with its appendix tables
+ * (thelatestinai.com).
+ *
  * The method (SPLASH, weekinpapers page, Abstract) rests on attention with few
  * or no KV heads: every query head of a request attends to one shared latent
  * KV row per token, so where a request's cache lives is independent of how the

@@ -33,6 +33,11 @@
 // MFMAs: the softmax runs while the matrix cores work.
 // A chunk writes normalised O and LSE (to the caller's output, or to the
 // split-KV workspace that splash_lse_merge then combines).
+//
+// Pages cited: the weekinpapers page is "SPLASH: Switching Parallel Layouts of
+// Attention with Seamless Handoff for LLM Serving" (weekinpapers.com); the
+// thelatestinai page is that paper's summary with its appendix tables
+// (thelatestinai.com).
 #include <type_traits>
 
 #include "common.h"

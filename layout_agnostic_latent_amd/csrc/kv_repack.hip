@@ -4,6 +4,11 @@
 // (weekinpapers page, Abstract: the state not already in place is moved in the
 // background and handed off at a batch boundary).  A pure bandwidth copy;
 // bit-exact by construction.
+//
+// Pages cited: the weekinpapers page is "SPLASH: Switching Parallel Layouts of
+// Attention with Seamless Handoff for LLM Serving" (weekinpapers.com); the
+// thelatestinai page is that paper's summary with its appendix tables
+// (thelatestinai.com).
 #include "common.h"
 
 namespace splash {

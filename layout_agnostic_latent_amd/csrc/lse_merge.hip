@@ -3,6 +3,11 @@
 // holds 1/T of every history) and of split-KV within one rank.  Per row:
 //   M = max_p L_p,  L = M + log(sum_p exp(L_p - M)),  O = sum_p exp(L_p - L) O_p.
 // HBM-bound: each partial value is read once, each output written once.
+//
+// Pages cited: the weekinpapers page is "SPLASH: Switching Parallel Layouts of
+// Attention with Seamless Handoff for LLM Serving" (weekinpapers.com); the
+// thelatestinai page is that paper's summary with its appendix tables
+// (thelatestinai.com).
 #include "common.h"
 
 namespace splash {

@@ -22,6 +22,10 @@ The model therefore cannot reproduce the pages' end-to-end crossovers at
 short inputs (Tables 4-6), where sharded weight reads favour TP; it shows the
 attention side, where reading every history on every rank makes TP lose as
 contexts grow.
+
+Pages cited: the weekinpapers page is "SPLASH: Switching Parallel Layouts of Attention with
+Seamless Handoff for LLM Serving" (weekinpapers.com); the thelatestinai page is that paper's
+summary with its appendix tables (thelatestinai.com).
 """
 from __future__ import annotations
 

@@ -39,6 +39,11 @@ layout-invariance of all three shares, brute force in pure Python / mpmath on
 tiny inputs, page-permutation invariance, bounds, the merge identities, and the
 busiest-rank loads of Table 2 (tests/golden/table2_loads.json).  No function
 here is "parity unpinned".
+
+Pages cited: the weekinpapers page is "SPLASH: Switching Parallel Layouts of Attention with
+Seamless Handoff for LLM Serving" (weekinpapers.com); the thelatestinai page is that paper's
+summary with its appendix tables (thelatestinai.com); the zot.news page is "Decoupling attention
+from model weights speeds large-language-model serving by up to 2x" (zot.news).
 """
 from __future__ import annotations
 

@@ -22,6 +22,10 @@ Conventions
   references are filled with a quiet-NaN bit pattern, so any read of them that
   is not masked shows up in the result.
 * Every tensor of a case gets its own child of ``SeedSequence(seed)``.
+
+Pages cited: the weekinpapers page is "SPLASH: Switching Parallel Layouts of Attention with
+Seamless Handoff for LLM Serving" (weekinpapers.com); the thelatestinai page is that paper's
+summary with its appendix tables (thelatestinai.com).
 """
 from __future__ import annotations
 
