@@ -14,11 +14,11 @@
  * attention weights are sharded.  A layout is then only a choice of share
  * (thelatestinai page, Appendix Table 2 and its caption):
  *   TP            a slice of the query heads, every request's whole history;
- *   CP            a contiguous token range of every request ("ideal token
- *                 partitioning"), emitted as partial output + log-sum-exp and
- *                 merged afterwards;
- *   DP-attention  the whole histories of the requests a rank owns
- *   and DOP       ("count-balanced request ownership").
+ *   CP            a contiguous token range of every request, the tokens
+ *                 split evenly over the ranks, emitted as partial output +
+ *                 log-sum-exp and merged afterwards;
+ *   DP-attention  the whole histories of the requests a rank owns, the
+ *   and DOP       requests dealt to the ranks in equal numbers.
  * One call of splash_decode_attn computes any of these shares: a head range,
  * a token range and the set of requests in the batch passed to the call.
  * splash_lse_merge combines partial results over disjoint token ranges (the
@@ -89,7 +89,8 @@ typedef struct splash_desc {
  *
  *   q            bf16 [num_reqs][num_heads][d_qk], rows contiguous
  *   kv_pages     bf16 [num_pages][page_size][G][d_qk] (G = num_kv_heads; the
- *                premise is attention with few or no KV heads, weekinpapers
+ *                premise is attention whose query heads share one or a few
+ *                KV heads, weekinpapers
  *                page, Abstract: G = 1 is the latent-KV case, G > 1 groups
  *                the query heads onto a few shared KV heads)
  *   block_table  int32 [num_reqs][max_pages_per_req]; only the entries that

@@ -5,9 +5,9 @@
 // Appendix Table 2): TP = head slice over whole histories, CP = token range of
 // every history with partial output + LSE, DP-attention / DOP = whole owned
 // requests.  Every query head of a request attends to the same latent row per
-// token (weekinpapers page, Abstract: attention with few or no KV heads), and
-// V is the first d_v dims of that row, so one LDS tile of KV rows feeds both
-// contractions.
+// token (weekinpapers page, Abstract: query heads sharing one or a few KV
+// heads), and V is the first d_v dims of that row, so one LDS tile of KV rows
+// feeds both contractions.
 //
 // Work decomposition.  A workgroup owns (request b, a chunk of 32-token tiles,
 // a group of up to 32*WH heads).  Its WH*WV waves each hold 32 heads:

@@ -8,16 +8,16 @@ input generators of ``workloads``.
 
 What is computed, and where the pages fix it
 --------------------------------------------
-SPLASH (weekinpapers page, Abstract) rests on attention "with few or no KV
-heads": every query head of a request attends to one shared latent KV row per
+SPLASH (weekinpapers page, Abstract) rests on attention whose query heads
+share one or a few KV heads: every query head of a request attends to one shared latent KV row per
 token, so where a request's cache lives is independent of how the attention
 weights are sharded.  One rank's share of a decode step is then
 
 * a slice of the query heads over every request's whole history (TP),
 * a contiguous token range of every request, emitted as a partial output plus
-  its log-sum-exp and merged afterwards (CP, "ideal token partitioning"),
+  its log-sum-exp and merged afterwards (CP, tokens split evenly),
 * or the whole histories of the requests the rank owns (DP-attention, DOP,
-  "count-balanced request ownership"),
+  requests dealt to the ranks in equal numbers),
 
 as laid out in thelatestinai page, Appendix Table 2 and its caption.  The
 merge of partial results across ranks is the cross-node attention merge that
@@ -83,7 +83,7 @@ def decode_attn(q: np.ndarray, kv_pages: np.ndarray, block_table: np.ndarray,
       s_t = scale * q[b,h] . k_t
       O   = sum_t exp(s_t - m) v_t / sum_t exp(s_t - m),  m = max_t s_t
       LSE = m + log(sum_t exp(s_t - m))
-    The premise is attention with few or no KV heads (weekinpapers page,
+    The premise is attention whose query heads share one or a few KV heads (weekinpapers page,
     Abstract); with G > 1 the query heads are taken to share KV heads in
     contiguous groups of H / G.
     """
@@ -176,9 +176,9 @@ def layout_shares(layout: str, B: int, T: int, s: int, H: int) -> List[Dict]:
     Each share is {'reqs': [...], 'heads': (lo, hi), 'toks': (lo, hi)}.
     * TP: rank r holds heads [r*H/T, (r+1)*H/T) of every request, all tokens.
     * CP: rank r holds tokens [r*s/T, (r+1)*s/T) of every request, all heads
-      ("ideal token partitioning").
+      (the tokens split evenly over the ranks).
     * DP-attention and DOP: requests are dealt to owners by count (request b
-      to rank b mod T, "count-balanced request ownership"); each owner holds
+      to rank b mod T, equal numbers per rank); each owner holds
       all heads and all tokens of its requests.  DOP differs from DP-attention
       only in how the weights are sharded, not in the attention share.
     """
