@@ -168,29 +168,63 @@ __device__ int4 plan_item(const DecodeArgs& a, int32_t* scratch) {
   const long long full_cap = (long long)a.plan_target * a.plan_max_chunk;
   int chunk = total >= full_cap ? a.plan_max_chunk
                                 : max(a.plan_min_chunk, ((int)total + a.plan_target - 1) / a.plan_target);
-  if (chunk < a.plan_max_chunk) {
-    // Items with chunk length c: sum over requests of ceil(tiles / c), a
-    // block-wide count (every thread gets the same value).
-    int* cnt = scratch + 2 * NWV + 8;  // [NWV], clear of red[]
-    auto items_at = [&](int c) -> int {
-      int m = 0;
-      for (int k = 0; k < per; ++k) {
-        const int r = tid * per + k;
-        if (r < a.num_reqs) m += (tiles(r) + c - 1) / c;
+  // Per thread: full chunks nf and remainder chunks nr of its requests at
+  // chunk length c; their inclusive prefix over the wave (fi, ri), the
+  // prefix before this wave (fb, rb) and the totals (F, R).  wsum: LDS,
+  // [NWV][2], clear of red[].
+  int* wsum = scratch + 2 * NWV + 8;
+  int* mine_item = scratch + 4 * NWV + 16;  // [4]: this workgroup's item
+  if (tid == 0) mine_item[0] = -1;          // ordered by the barrier below
+  int nf = 0, nr = 0, fi = 0, ri = 0, fb = 0, rb = 0, F = 0, R = 0;
+  auto count_items = [&](int c) {
+    nf = 0;
+    nr = 0;
+    for (int k = 0; k < per; ++k) {
+      const int r = tid * per + k;
+      if (r < a.num_reqs) {
+        const int nt = tiles(r);
+        nf += nt / c;
+        nr += (nt % c) ? 1 : 0;
       }
-      for (int d = 32; d >= 1; d >>= 1) m += __shfl_xor(m, d, 64);
-      if (lane == 0) cnt[wave] = m;
-      __syncthreads();
-      int n = 0;
-      for (int w = 0; w < NWV; ++w) n += cnt[w];
-      __syncthreads();
-      return n;
+    }
+    fi = nf;
+    ri = nr;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int uf = __shfl_up(fi, d, 64), ur = __shfl_up(ri, d, 64);
+      if (lane >= d) {
+        fi += uf;
+        ri += ur;
+      }
+    }
+    if (lane == 63) {
+      wsum[2 * wave] = fi;
+      wsum[2 * wave + 1] = ri;
+    }
+    __syncthreads();
+    fb = rb = F = R = 0;
+    for (int w = 0; w < NWV; ++w) {
+      if (w < wave) {
+        fb += wsum[2 * w];
+        rb += wsum[2 * w + 1];
+      }
+      F += wsum[2 * w];
+      R += wsum[2 * w + 1];
+    }
+  };
+  count_items(chunk);
+  // A ragged batch's remainder chunks can overflow one round of plan_target
+  // workgroups (F + R items); the items past it then start only when earlier
+  // ones end, which can double the critical path.  Take the shortest chunk
+  // that fits one round instead, if any chunk up to the maximum does.  Items
+  // at length c are the sum over requests of ceil(tiles / c), a block-wide
+  // count; uniform batches fit at the first length and never count again.
+  if (F + R > a.plan_target && chunk < a.plan_max_chunk) {
+    auto items_at = [&](int c) -> int {
+      __syncthreads();  // every thread has read wsum before it is rewritten
+      count_items(c);
+      return F + R;
     };
-    // A ragged batch's remainder chunks can overflow one round of plan_target
-    // workgroups; the items past it then start only when earlier ones end,
-    // which can double the critical path.  Take the shortest chunk that fits
-    // one round instead, if any chunk up to the maximum does.
-    if (items_at(chunk) > a.plan_target && items_at(a.plan_max_chunk) <= a.plan_target) {
+    if (items_at(a.plan_max_chunk) <= a.plan_target) {
       int lo = chunk, hi = a.plan_max_chunk;  // items_at(lo) > target >= items_at(hi)
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -199,40 +233,8 @@ __device__ int4 plan_item(const DecodeArgs& a, int32_t* scratch) {
       }
       chunk = hi;
     }
-  }
-  int nf = 0, nr = 0;
-  for (int k = 0; k < per; ++k) {
-    const int r = tid * per + k;
-    if (r < a.num_reqs) {
-      const int nt = tiles(r);
-      nf += nt / chunk;
-      nr += (nt % chunk) ? 1 : 0;
-    }
-  }
-  int fi = nf, ri = nr;  // inclusive prefix within the wave
-  for (int d = 1; d < 64; d <<= 1) {
-    const int uf = __shfl_up(fi, d, 64), ur = __shfl_up(ri, d, 64);
-    if (lane >= d) {
-      fi += uf;
-      ri += ur;
-    }
-  }
-  int* wsum = scratch + 2 * NWV + 8;  // [NWV][2], clear of red[]
-  if (lane == 63) {
-    wsum[2 * wave] = fi;
-    wsum[2 * wave + 1] = ri;
-  }
-  int* mine_item = scratch + 4 * NWV + 16;  // [4]
-  if (tid == 0) mine_item[0] = -1;
-  __syncthreads();
-  int fb = 0, rb = 0, F = 0, R = 0;
-  for (int w = 0; w < NWV; ++w) {
-    if (w < wave) {
-      fb += wsum[2 * w];
-      rb += wsum[2 * w + 1];
-    }
-    F += wsum[2 * w];
-    R += wsum[2 * w + 1];
+    __syncthreads();
+    count_items(chunk);
   }
   int foff = fb + fi - nf;
   int rnext = F + rb + ri - nr;
