@@ -154,10 +154,17 @@ __device__ int4 plan_item(const DecodeArgs& a, int32_t* scratch) {
     const int h = min(min(a.tok_hi, a.seq_lens[r]), cap);
     return h > lo ? (h + kTileTok - 1) / kTileTok - first : 0;
   };
+  // Each pass below visits this thread's requests: f(r, tiles of r).  With
+  // one request per thread (batches of up to NT requests) its tiles are
+  // loaded once, into a register; re-reading seq_lens after each barrier
+  // would put a dependent memory round trip into every pass.
+  const bool cached = per == 1;
+  const int tcache = (cached && tid < a.num_reqs) ? tiles(tid) : 0;
+  auto tiles_k = [&](int r) -> int { return cached ? tcache : tiles(r); };  // r = tid * per + k
   long long mine = 0;
   for (int k = 0; k < per; ++k) {
     const int r = tid * per + k;
-    if (r < a.num_reqs) mine += tiles(r);
+    if (r < a.num_reqs) mine += tiles_k(r);
   }
   for (int d = 32; d >= 1; d >>= 1) mine += __shfl_xor(mine, d, 64);
   long long* red = (long long*)scratch;  // [NWV]
@@ -182,7 +189,7 @@ __device__ int4 plan_item(const DecodeArgs& a, int32_t* scratch) {
     for (int k = 0; k < per; ++k) {
       const int r = tid * per + k;
       if (r < a.num_reqs) {
-        const int nt = tiles(r);
+        const int nt = tiles_k(r);
         nf += nt / c;
         nr += (nt % c) ? 1 : 0;
       }
@@ -240,10 +247,10 @@ __device__ int4 plan_item(const DecodeArgs& a, int32_t* scratch) {
   int rnext = F + rb + ri - nr;
   const int me = blockIdx.x;
   const bool writer = blockIdx.x == 0 && blockIdx.z == 0;
-  for (int k = 0; k < per; ++k) {
+  for (int k = 0; k < per; ++k) {  // in request order: foff and rnext accumulate
     const int r = tid * per + k;
     if (r >= a.num_reqs) break;
-    const int nt = tiles(r);
+    const int nt = tiles_k(r);
     const int nfull = nt / chunk;
     const int rslot = (nt % chunk) ? rnext++ : -1;
     if (me >= foff && me < foff + nfull) {
