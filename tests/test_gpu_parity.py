@@ -507,3 +507,52 @@ def test_measure_peaks_is_plausible():
     assert 500.0 < pk["hbm_read_gbps"] < 20000.0
     with pytest.raises(sp.SplashError):
         sp.measure_peaks(buf[:1000])   # under 1 MiB
+
+
+# ---------------------------------------------------------------------------
+# HIP graph replay of a step (decode with its split-KV merge, then a repack)
+# ---------------------------------------------------------------------------
+def test_graph_replay_matches_eager():
+    """The step captured into a HIP graph: every replay, with eager work and
+    synchronisations between replays, equals the eager result bit for bit."""
+    c = W.case_owner(B=4, ctx=2048)
+    t = to_dev(c)
+    rc = W.make_repack_case(c, seed=11)
+    st, dt = torch.from_numpy(rc.src_table).to(DEV), torch.from_numpy(rc.dst_table).to(DEV)
+    fill = int(np.int16(rc.dst_fill.view(np.int16)))
+    shape = (rc.dst_num_pages,) + c.kv_pages.shape[1:]
+    hs = c.num_q_heads
+
+    def run(out, lse, dst):
+        sp.decode_attn(t["q"], t["kv"], t["bt"], t["sl"], c.head_lo, c.head_hi, c.tok_lo, c.tok_hi, out, lse,
+                       d_v=c.d_v, scale=c.scale)
+        sp.kv_repack(t["kv"], st, dst, dt)
+
+    out_e = torch.empty((c.num_reqs, hs, c.d_v), dtype=torch.float32, device=DEV)
+    lse_e = torch.empty((c.num_reqs, hs), dtype=torch.float32, device=DEV)
+    dst_e = torch.full(shape, fill, dtype=torch.int16, device=DEV)
+    run(out_e, lse_e, dst_e)   # eager; also sizes the split-KV workspace before capture
+    torch.cuda.synchronize()
+
+    out_g, lse_g = torch.empty_like(out_e), torch.empty_like(lse_e)
+    dst_g = torch.full(shape, fill, dtype=torch.int16, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(out_g, lse_g, dst_g)
+    torch.cuda.synchronize()
+    scratch_o, scratch_l = torch.empty_like(out_e), torch.empty_like(lse_e)
+    for r in range(3):
+        out_g.fill_(float("nan"))
+        lse_g.fill_(float("nan"))
+        dst_g.fill_(fill)
+        torch.cuda.synchronize()
+        g.replay()
+        # eager work of the program between replays
+        sp.decode_attn(t["q"], t["kv"], t["bt"], t["sl"], c.head_lo, c.head_hi, 0, 1000, scratch_o, scratch_l,
+                       d_v=c.d_v, scale=c.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {r}: output differs from eager"
+        assert torch.equal(lse_g, lse_e), f"replay {r}: LSE differs from eager"
+        assert torch.equal(dst_g, dst_e), f"replay {r}: repack differs from eager"
+    ro, rl = run_oracle(c)
+    assert_close(out_g.cpu().double().numpy(), lse_g.cpu().double().numpy(), ro, rl, what="graph replay")
