@@ -27,6 +27,7 @@ import hashlib
 import json
 import os
 import statistics
+import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -106,7 +107,48 @@ def read_pmc(d, counter):
     return vals
 
 
+def counters_main(argv) -> None:
+    """--counters mode: a table of the decode kernel's per-dispatch counter
+    averages for several runs (one rocprofv3 --pmc output directory each)."""
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--counters", action="store_true")
+    ap.add_argument("--name", required=True)
+    ap.add_argument("--command", required=True, action="append")
+    ap.add_argument("--run", required=True, action="append", nargs=3, metavar=("LABEL", "DIR", "ALG_FLOPS"),
+                    help="workload label, rocprofv3 output directory, algorithmic FLOPs per decode call")
+    args = ap.parse_args(argv)
+    rows = []
+    for label, d, alg in args.run:
+        vals = defaultdict(list)
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                if "decode_attn_kernel" in row["Kernel_Name"]:
+                    vals[row["Counter_Name"]].append(float(row["Counter_Value"]))
+        rows.append((label, float(alg), {k: statistics.mean(v) for k, v in vals.items()}))
+    names = sorted({k for _, _, v in rows for k in v})
+    lines = [f"# {args.name}", "", "Produced by:", ""] + [f"    {c}" for c in args.command]
+    lines += ["", f"Kernel source hash: `{kernel_source_hash()}`", "",
+              "Per decode_attn_kernel dispatch (average over the run's dispatches):", "",
+              "| workload | " + " | ".join(names) + " | MFMA FLOPs / algorithmic | LDS conflict share |",
+              "|---|" + "---|" * (len(names) + 2)]
+    for label, alg, v in rows:
+        fl = v.get("MfmaFlopsBF16")
+        bank, active = v.get("SQ_LDS_BANK_CONFLICT"), v.get("SQ_LDS_IDX_ACTIVE")
+        share = (bank / (active - bank)) if bank is not None and active and active > bank else None
+        cells = [f"{v[n]:.6g}" if n in v else "" for n in names]
+        lines.append(f"| {label} | " + " | ".join(cells) + f" | {'' if fl is None else f'{fl / alg:.3f}'} | "
+                     f"{'' if share is None else f'{100 * share:.2f}%'} |")
+    lines += ["", "MfmaUtil: MFMA busy cycles over (active cycles x SIMDs), percent. MfmaFlopsBF16: 512 x the "
+              "bf16 MFMA op count. LDS conflict share: bank-conflict cycles over conflict-free LDS cycles."]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, args.name + ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
+    if "--counters" in sys.argv[1:]:
+        return counters_main(sys.argv[1:])
     ap = argparse.ArgumentParser()
     ap.add_argument("--name", required=True)
     ap.add_argument("--command", required=True, action="append", help="command(s) that produced the data")
