@@ -272,6 +272,70 @@ __device__ int4 plan_item(const DecodeArgs& a, int32_t* scratch) {
   return it;
 }
 
+// The same plan for batches of at most 64 requests, computed by every wave
+// on its own: request r's tile count sits in lane r, and every sum, prefix
+// and search is a wave reduction, so the plan needs no LDS and no barrier.
+// Gives the same items as plan_item.
+__device__ int4 plan_item_wave(const DecodeArgs& a) {
+  const int lane = threadIdx.x & 63;
+  const int lo = max(a.tok_lo, 0);
+  const int first = lo / kTileTok;
+  const int cap = a.max_pages << a.page_shift;
+  int nt = 0;  // tiles of request `lane`
+  if (lane < a.num_reqs) {
+    const int h = min(min(a.tok_hi, a.seq_lens[lane]), cap);
+    nt = h > lo ? (h + kTileTok - 1) / kTileTok - first : 0;
+  }
+  auto wsum = [](int v) {
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
+  };
+  long long total = nt;
+  for (int d = 32; d >= 1; d >>= 1) total += __shfl_xor(total, d, 64);
+  const long long full_cap = (long long)a.plan_target * a.plan_max_chunk;
+  int chunk = total >= full_cap ? a.plan_max_chunk
+                                : max(a.plan_min_chunk, ((int)total + a.plan_target - 1) / a.plan_target);
+  auto items_at = [&](int c) { return wsum(nt / c + ((nt % c) ? 1 : 0)); };
+  // a ragged batch whose items overflow one round takes the shortest chunk
+  // that fits, if any chunk up to the maximum does (as plan_item)
+  if (items_at(chunk) > a.plan_target && chunk < a.plan_max_chunk && items_at(a.plan_max_chunk) <= a.plan_target) {
+    int lo_c = chunk, hi_c = a.plan_max_chunk;  // items_at(lo_c) > target >= items_at(hi_c)
+    while (hi_c - lo_c > 1) {
+      const int mid = (lo_c + hi_c) >> 1;
+      if (items_at(mid) <= a.plan_target) hi_c = mid;
+      else lo_c = mid;
+    }
+    chunk = hi_c;
+  }
+  // full chunks numbered in request order, then one remainder per request
+  const int nf = nt / chunk, nr = (nt % chunk) ? 1 : 0;
+  int fi = nf, ri = nr;  // inclusive prefix sums over the requests
+  for (int d = 1; d < 64; d <<= 1) {
+    const int uf = __shfl_up(fi, d, 64), ur = __shfl_up(ri, d, 64);
+    if (lane >= d) {
+      fi += uf;
+      ri += ur;
+    }
+  }
+  const int F = __shfl(fi, 63, 64);
+  const int foff = fi - nf;
+  const int rslot = nr ? F + ri - nr : -1;
+  const int me = blockIdx.x;
+  if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x < 64 && lane < a.num_reqs)
+    a.req_info[lane] = make_int4(foff, nf, rslot, 0);
+  const bool mine = lane < a.num_reqs && ((me >= foff && me < foff + nf) || me == rslot);
+  const unsigned long long bal = __ballot(mine);
+  if (bal == 0) return make_int4(-1, 0, 0, me);
+  const int r = __ffsll((long long)bal) - 1;  // the one request holding item me
+  const int r_foff = __builtin_amdgcn_readlane(foff, r);
+  const int r_nf = __builtin_amdgcn_readlane(nf, r);
+  const int r_nt = __builtin_amdgcn_readlane(nt, r);
+  const bool full = me < r_foff + r_nf;
+  const int t0 = full ? first + (me - r_foff) * chunk : first + r_nf * chunk;
+  const int t1 = full ? t0 + chunk : first + r_nt;
+  return make_int4(r, __builtin_amdgcn_readfirstlane(t0), __builtin_amdgcn_readfirstlane(t1), me);
+}
+
 template <int D_QK, int D_V, int WH, int WV>
 struct Cfg {
   static constexpr int NW = WH * WV;
@@ -337,7 +401,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   int4 item = make_int4(0, 0, 0, 0);
   const bool worklist = a.plan_target > 0;
   if (worklist) {
-    item = plan_item<C::NTHREADS>(a, page_lds);
+    item = a.num_reqs <= 64 ? plan_item_wave(a) : plan_item<C::NTHREADS>(a, page_lds);
     if (item.x < 0) return;  // beyond the plan's items
     b = item.x;
     split = item.w;
