@@ -2,9 +2,11 @@
 """Throughput of one rank's decode-attention share over a paged latent KV head
 on one MI355X, through libsplash_attn's C ABI.
 
-Default workload: the request-owned share of a DP-attention / DOP owner,
-B=16 requests x 4,096 tokens, 128 query heads sharing one latent KV row of
-576 bf16 dims (V = the first 512), page size 64, randomly permuted pages.
+Default workload: the transition batch, the largest single-GPU case: 64
+requests with context lengths drawn log-uniform in [512, 65,536] (856,942 KV
+tokens), 128 query heads sharing one latent KV row of 576 bf16 dims (V = the
+first 512), page size 64, randomly permuted pages, each request owned whole
+(the DP-attention / DOP owner share).
 One step = one pass of the whole hot path over one batch:
   * splash_decode_attn over the batch (split-KV chunks + their merge), and
   * splash_kv_repack of a seeded half of the batch's requests (all their
@@ -42,7 +44,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="owner",
+    ap.add_argument("--workload", default="transition",
                     help="owner | tp | cp | transition | sweep:<owner|tp|cp|gqa<G>>:<ctx>")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
@@ -212,15 +214,20 @@ def main():
         buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         buf.fill_(1)
         pk = sp.measure_peaks(buf)
+        copy_gbps = device_copy_rate(buf)
         del buf
         dec_tflops = dec_flops / (dec_us * 1e-6) / 1e12
         peaks = {"mfma_bf16_TFLOPs": round(pk["mfma_bf16_tflops"], 1),
                  "mfma_clock_GHz": round(pk["mfma_clock_ghz"], 3),
                  "hbm_read_GBps": round(pk["hbm_read_gbps"], 1),
+                 "copy_rw_GBps": round(copy_gbps, 1),
                  "decode_frac_of_measured_read": round(achieved / pk["hbm_read_gbps"], 4),
                  "decode_frac_of_measured_mfma": round(dec_tflops / pk["mfma_bf16_tflops"], 4),
                  "how": "splash_measure_peaks: v_mfma_f32_32x32x16_bf16 loop on every SIMD (~2 ms, best of 3), "
-                        "shader clock from s_memtime / s_memrealtime; non-temporal streaming read of 1 GiB"}
+                        "shader clock from s_memtime / s_memrealtime; non-temporal streaming read of 1 GiB; "
+                        "copy_rw_GBps: torch's device-to-device copy of 512 MiB (read + write bytes), best of 5"}
+        if rep is not None:
+            peaks["repack_frac_of_measured_copy"] = round(parts["repack_TBps_rw"] * 1e3 / copy_gbps, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -249,6 +256,7 @@ def main():
         "parts": parts,
         "measured_peaks": peaks,
         "cpu_baseline": cpu,
+        "library": sp.library_info(),
     }
     print(json.dumps(line), flush=True)
 
@@ -431,6 +439,25 @@ def run_layout_model(args, B=16, T=8, H=128, contexts=(1024, 4096, 16384, 32768,
         "rows": rows,
     }
     print(json.dumps(line))
+
+
+def device_copy_rate(buf):
+    """Read + write GB/s of torch's device-to-device copy between the two
+    halves of `buf` (best of 5), the box's own copy rate next to the 8 TB/s
+    published peak."""
+    import torch
+    half = buf.numel() // 2
+    a, b = buf[:half], buf[half:2 * half]
+    b.copy_(a)
+    best = float("inf")
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    return 2 * half / (best * 1e-3) / 1e9
 
 
 def measured_traffic(workload, kernel_prefix):

@@ -100,14 +100,20 @@ typedef struct splash_desc {
  *   out          fp32 [num_reqs][head_hi - head_lo][d_v]
  *   lse          fp32 [num_reqs][head_hi - head_lo], or NULL
  * The work is split into KV chunks (split-KV) when the share is too small to
- * fill the GPU; partials then go to a library-owned workspace (allocated on
- * first need, grown on demand, freed by splash_release_workspace) and are
- * merged on the same stream.  A partial output is kept in fp16 (its LSE in
- * fp32) between the two kernels; a value beyond the fp16 range is clamped and
- * raises SPLASH_DEVERR_PARTIAL_RANGE.  Every KV head the share touches is served by
- * the same launch (one decode kernel, plus one merge kernel when split).
- * Growing the workspace synchronises the device,
- * so a call that needs more workspace must not be made under stream capture.
+ * fill the GPU; partials then go to a library-owned workspace and are merged
+ * on the same stream.  A partial output is kept in fp16 (its LSE in fp32)
+ * between the two kernels; a value beyond the fp16 range is clamped and
+ * raises SPLASH_DEVERR_PARTIAL_RANGE.  Every KV head the share touches is
+ * served by the same launch (one decode kernel, plus one merge kernel when
+ * split).
+ * Workspace: one per (device, stream), allocated on first need and grown on
+ * demand (growth synchronises that stream, then frees the old buffer), freed
+ * by splash_release_workspace.  Calls on different streams therefore never
+ * share partials.  Under stream capture a call may use its stream's
+ * workspace but not grow it: it then returns SPLASH_EINVAL (make one eager
+ * call of the same share on the capturing stream first).  A captured graph
+ * keeps the workspace's address, so growing that stream's workspace later or
+ * calling splash_release_workspace invalidates such graphs.
  * Errors: SPLASH_EINVAL for null pointers, non-positive sizes, head range
  * outside [0, num_heads) or empty, tok_hi < tok_lo, num_kv_heads < 0 or not
  * dividing num_heads; SPLASH_EUNSUPPORTED for
@@ -162,7 +168,8 @@ const char* splash_last_error(void);
  */
 int splash_device_errors(int32_t* flags, int32_t clear);
 
-/* Free the split-KV workspace of the current device (synchronises it). */
+/* Free every split-KV workspace of the current device (synchronises it).
+ * Graphs captured with a split-KV call on this device become invalid. */
 int splash_release_workspace(void);
 
 /*

@@ -16,13 +16,19 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["LIB_PATH", "SplashError", "lib", "decode_attn", "decode_plan", "lse_merge", "kv_repack",
+__all__ = ["LIB_PATH", "SplashError", "lib", "library_info", "decode_attn", "decode_plan", "lse_merge", "kv_repack",
            "device_errors", "release_workspace", "profile_start", "profile_stop", "measure_peaks", "DEVERR_BAD_PAGE",
            "DEVERR_REPACK_PAIR", "DEVERR_PARTIAL_RANGE"]
 
-# The in-tree build; SPLASH_LIB may name another build of the same library.
-LIB_PATH = os.environ.get("SPLASH_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                                                         "libsplash_attn.so")
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+# The in-tree build.  SPLASH_LIB may only name a library inside this package
+# (so that a result can never come from a build made elsewhere).
+LIB_PATH = os.path.join(_PKG_DIR, "libsplash_attn.so")
+if os.environ.get("SPLASH_LIB"):
+    _alt = os.path.realpath(os.environ["SPLASH_LIB"])
+    if os.path.dirname(_alt) != os.path.realpath(_PKG_DIR):
+        raise ImportError(f"SPLASH_LIB={os.environ['SPLASH_LIB']} is outside the package directory {_PKG_DIR}")
+    LIB_PATH = _alt
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
 DEVERR_BAD_PAGE, DEVERR_REPACK_PAIR, DEVERR_PARTIAL_RANGE = 1, 2, 4
@@ -89,6 +95,14 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+def library_info() -> dict:
+    """Path and SHA-256 (first 16 hex digits) of the library file this process loads."""
+    import hashlib
+    with open(LIB_PATH, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    return {"path": os.path.relpath(LIB_PATH, os.path.dirname(_PKG_DIR)), "sha256_16": digest}
+
+
 def _check(rc: int) -> None:
     if rc != OK:
         raise SplashError(rc, lib().splash_last_error().decode())
@@ -139,6 +153,12 @@ def decode_attn(q, kv_pages, block_table, seq_lens, head_lo: int, head_hi: int, 
     """splash_decode_attn.  q bf16 [B,H,d_qk]; kv_pages bf16 [P,ps,d_qk] or [P,ps,G,d_qk] (G shared KV heads);
     block_table int32 [B,max_pages]; seq_lens int32 [B]; out fp32 [B, head_hi-head_lo, d_v];
     lse fp32 [B, head_hi-head_lo] or None."""
+    _decode("splash_decode_attn", q, kv_pages, block_table, seq_lens, head_lo, head_hi, tok_lo, tok_hi, out, lse,
+            d_v, scale, num_splits, stream)
+
+
+def _decode(entry, q, kv_pages, block_table, seq_lens, head_lo, head_hi, tok_lo, tok_hi, out, lse, d_v, scale,
+            num_splits, stream):
     import torch
     bf = (torch.bfloat16, torch.int16, torch.uint16)
     _require(q, "q", bf, 3)
@@ -155,8 +175,8 @@ def decode_attn(q, kv_pages, block_table, seq_lens, head_lo: int, head_hi: int, 
     if block_table.shape[0] != B or seq_lens.shape[0] != B:
         raise ValueError("block_table / seq_lens rows != B")
     d = _desc_from(q, kv_pages, block_table, d_v, scale, num_splits)
-    _check(lib().splash_decode_attn(ctypes.byref(d), _ptr(q), _ptr(kv_pages), _ptr(block_table), _ptr(seq_lens),
-                                    head_lo, head_hi, tok_lo, tok_hi, _ptr(out), _ptr(lse), _stream(stream)))
+    _check(getattr(lib(), entry)(ctypes.byref(d), _ptr(q), _ptr(kv_pages), _ptr(block_table), _ptr(seq_lens),
+                                 head_lo, head_hi, tok_lo, tok_hi, _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def decode_plan(num_reqs, num_heads, d_qk, d_v, page_size, max_pages_per_req, num_pages, scale,
@@ -188,12 +208,23 @@ def lse_merge(partials, lses, out, lse_out=None, *, stream=None) -> None:
 def kv_repack(src_pages, src_table, dst_pages, dst_table, err_count=None, *, stream=None) -> None:
     """splash_kv_repack over whole pages (the leading dim of src_pages / dst_pages)."""
     import torch
+    for name, pool in (("src_pages", src_pages), ("dst_pages", dst_pages)):
+        if not isinstance(pool, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if not pool.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+        if not pool.is_contiguous() or pool.dim() < 1:
+            raise ValueError(f"{name} must be a contiguous tensor of pages (leading dimension)")
+    if src_pages.device != dst_pages.device:
+        raise ValueError("src_pages and dst_pages are on different devices")
+    if src_pages.dtype != dst_pages.dtype:
+        raise TypeError(f"pool dtypes differ: {src_pages.dtype} and {dst_pages.dtype}")
     _require(src_table, "src_table", (torch.int32,), 2)
     _require(dst_table, "dst_table", (torch.int32,), 2)
+    if src_table.device != src_pages.device or dst_table.device != src_pages.device:
+        raise ValueError("the block tables must be on the pools' device")
     if tuple(src_table.shape) != tuple(dst_table.shape):
         raise ValueError("src_table and dst_table shapes differ")
-    if not (src_pages.is_contiguous() and dst_pages.is_contiguous()):
-        raise ValueError("pools must be contiguous")
     page_bytes = src_pages[0].numel() * src_pages.element_size() if src_pages.shape[0] else \
         (dst_pages[0].numel() * dst_pages.element_size())
     dst_page_bytes = dst_pages[0].numel() * dst_pages.element_size() if dst_pages.shape[0] else page_bytes
@@ -201,6 +232,8 @@ def kv_repack(src_pages, src_table, dst_pages, dst_table, err_count=None, *, str
         raise ValueError("source and destination page sizes differ")
     if err_count is not None:
         _require(err_count, "err_count", (torch.int32,), 1)
+        if err_count.numel() < 1 or err_count.device != src_pages.device:
+            raise ValueError("err_count must hold at least one int32 on the pools' device")
     n, m = src_table.shape
     _check(lib().splash_kv_repack(_ptr(src_pages), _ptr(src_table), _ptr(dst_pages), _ptr(dst_table), n, m,
                                   page_bytes, src_pages.shape[0], dst_pages.shape[0], _ptr(err_count),

@@ -6,7 +6,6 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
-#include <string>
 #include <vector>
 
 #include "splash_attn.h"
@@ -23,15 +22,15 @@ constexpr int kMaxDevices = 64;
 constexpr int kNumCUs = 256;  // MI355X: 256 compute units in 8 XCDs
 constexpr int kMaxChunkTiles = 128;  // longest split-KV chunk (4,096 tokens)
 
-thread_local std::string t_last_error;
+// Message of the thread's last failing call (fixed size: reporting an error
+// allocates nothing).
+thread_local char t_last_error[512] = "";
 
 int fail(int code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vsnprintf(t_last_error, sizeof(t_last_error), fmt, ap);
   va_end(ap);
-  t_last_error = buf;
   return code;
 }
 
@@ -72,10 +71,17 @@ hipError_t timed(int kind, F&& launch) {
   return e;
 }
 
+// One split-KV workspace per (device, stream): calls on different streams
+// never share one, so their decode and merge kernels cannot overwrite each
+// other's partials.
+struct Workspace {
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
+};
 struct DeviceState {
   int32_t* dev_err = nullptr;  // address of g_splash_dev_err on this device
-  void* workspace = nullptr;
-  size_t workspace_bytes = 0;
+  std::vector<Workspace> ws;
 };
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
@@ -100,27 +106,46 @@ int device_error_word(int dev, int32_t** out) {
   return SPLASH_OK;
 }
 
-// Caller holds g_mu.  Grows (never shrinks) the split-KV workspace.
-int ensure_workspace(int dev, size_t bytes, void** out) {
+// Caller holds g_mu.  The split-KV workspace of `stream` on `dev`, grown
+// (never shrunk) to at least `bytes`.  Growing frees the old buffer after
+// the stream's work on it is done, so it is refused while the stream is
+// being captured into a graph (a captured kernel would keep the old
+// address).
+int ensure_workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
   DeviceState& st = g_dev[dev];
-  if (st.workspace_bytes < bytes) {
-    if (st.workspace) {
-      hipError_t e = hipDeviceSynchronize();  // kernels in flight may still use the old buffer
-      if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
-      e = hipFree(st.workspace);
-      st.workspace = nullptr;
-      st.workspace_bytes = 0;
+  Workspace* w = nullptr;
+  for (Workspace& x : st.ws)
+    if (x.stream == stream) w = &x;
+  if (!w) {
+    st.ws.push_back(Workspace{stream, nullptr, 0});
+    w = &st.ws.back();
+  }
+  if (w->bytes < bytes) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return fail_hip(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(SPLASH_EINVAL,
+                  "the split-KV workspace of this stream must grow to %zu bytes, which is not possible during "
+                  "stream capture: make one eager call of the same share on this stream first",
+                  bytes);
+    if (w->ptr) {
+      e = hipStreamSynchronize(stream);  // kernels in flight may still use the old buffer
+      if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+      e = hipFree(w->ptr);
+      w->ptr = nullptr;
+      w->bytes = 0;
       if (e != hipSuccess) return fail_hip(e, "hipFree(workspace)");
     }
     const size_t grown = bytes + bytes / 4;
-    hipError_t e = hipMalloc(&st.workspace, grown);
+    e = hipMalloc(&w->ptr, grown);
     if (e != hipSuccess) {
-      st.workspace = nullptr;
+      w->ptr = nullptr;
       return fail_hip(e, "hipMalloc(split-KV workspace)");
     }
-    st.workspace_bytes = grown;
+    w->bytes = grown;
   }
-  *out = st.workspace;
+  *out = w->ptr;
   return SPLASH_OK;
 }
 
@@ -309,7 +334,7 @@ using namespace splash;
 
 extern "C" {
 
-const char* splash_last_error(void) { return t_last_error.c_str(); }
+const char* splash_last_error(void) { return t_last_error; }
 
 int splash_decode_plan(const splash_desc* desc, int32_t head_lo, int32_t head_hi, int32_t tok_lo, int32_t tok_hi,
                        int32_t* num_splits, int32_t* head_groups, int64_t* workspace_bytes) {
@@ -373,7 +398,7 @@ int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, con
   }
   // split-KV: partials in the workspace, then the merge writes the caller's rows
   void* ws;
-  if ((rc = ensure_workspace(dev, (size_t)p.workspace_bytes, &ws))) return rc;
+  if ((rc = ensure_workspace(dev, stream, (size_t)p.workspace_bytes, &ws))) return rc;
   const int64_t rows = (int64_t)desc->num_reqs * hs;
   if (p.worklist) {
     const WorklistLayout w = worklist_layout(p.items_max, desc->num_reqs, hs, desc->d_v);
@@ -510,14 +535,15 @@ int splash_release_workspace(void) {
   if ((rc = current_device(&dev))) return rc;
   std::lock_guard<std::mutex> lock(g_mu);
   DeviceState& st = g_dev[dev];
-  if (st.workspace) {
-    hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
-    e = hipFree(st.workspace);
-    st.workspace = nullptr;
-    st.workspace_bytes = 0;
-    if (e != hipSuccess) return fail_hip(e, "hipFree(workspace)");
+  if (st.ws.empty()) return SPLASH_OK;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+  for (Workspace& w : st.ws) {
+    if (w.ptr && e == hipSuccess) e = hipFree(w.ptr);
+    w.ptr = nullptr;
   }
+  st.ws.clear();
+  if (e != hipSuccess) return fail_hip(e, "hipFree(workspace)");
   return SPLASH_OK;
 }
 

@@ -480,8 +480,10 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   const int l8 = lane >> 3;
   auto dma_inst = [&](int i) { return C::NW == 4 ? 4 * i + wave : wave * C::DMA_W + i; };
 
-  const int j0 = (t_begin * kTileTok) >> a.page_shift;
-  const int j1 = (mhi - 1) >> a.page_shift;  // last page holding a token of the chunk
+  // Pages holding a token of [mlo, mhi): only their block-table entries are
+  // read (a tile's rows below mlo fetch a row at or above it, see dma_plan).
+  const int j0 = mlo >> a.page_shift;
+  const int j1 = (mhi - 1) >> a.page_shift;
   // Where the tile loop finds the chunk's page ids (set up below, after the
   // first DMAs): 0 = the block table through the scalar cache, 1 = VGPRs
   // (page j0 + 64k + l in lane l of vpg[k]; read with v_readlane, no memory
@@ -520,10 +522,14 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   struct TilePages {
     int p0, p1;
   };
+  // Pages of rows 0..15 and 16..31 of tile t.  Rows below mlo take a row at
+  // or above it, so a half whose rows all lie below mlo is looked up at mlo
+  // (the page of the first row it is clamped to): no entry before the range
+  // is read.
   auto pages_of = [&](int t) -> TilePages {
     const int tok0 = t * kTileTok;
-    const int p0 = page_of(tok0);
-    const int p1 = (!one_page_per_tile && min(mhi - tok0, kTileTok) > 16) ? page_of(tok0 + 16) : p0;
+    const int p0 = page_of(max(tok0, mlo));
+    const int p1 = (!one_page_per_tile && min(mhi - tok0, kTileTok) > 16) ? page_of(max(tok0 + 16, mlo)) : p0;
     return {p0, p1};
   };
 

@@ -46,7 +46,7 @@ def run_oracle(case, head_lo=None, head_hi=None, tok_lo=None, tok_hi=None, reqs=
                               tok_lo, tok_hi, case.d_v, case.page_size, case.scale, reqs=reqs)
 
 
-def assert_close(go, gl, ro, rl, rows=None, what=""):
+def assert_close(go, gl, ro, rl, rows=None, what="", quiet=False):
     """Attention output within max-abs and relative-L2 bars, LSE within its bar.
 
     ``rows``: request indices to compare (default all).  -inf LSEs must match
@@ -66,8 +66,9 @@ def assert_close(go, gl, ro, rl, rows=None, what=""):
         if live.any():
             lerr = float(np.abs(gl[live] - rl[live]).max())
     # the margins, shown by `pytest -rP`
-    print(f"parity {what}: max abs {err:.2e} (bar {MAX_ABS:.0e}), rel L2 {rel:.2e} (bar {REL_L2:.0e}), "
-          f"LSE {lerr:.2e} (bar {LSE_ABS:.0e})", flush=True)
+    if not quiet:
+        print(f"parity {what}: max abs {err:.2e} (bar {MAX_ABS:.0e}), rel L2 {rel:.2e} (bar {REL_L2:.0e}), "
+              f"LSE {lerr:.2e} (bar {LSE_ABS:.0e})", flush=True)
     assert err <= MAX_ABS, f"{what}: max abs error {err:.3e}"
     assert rel <= REL_L2, f"{what}: relative L2 error {rel:.3e}"
     if gl is not None:

@@ -161,3 +161,31 @@ def test_measure_peaks_rejects_bad_arguments_without_a_gpu(splash):
     assert L.splash_measure_peaks(0x1000, 1000, ctypes.byref(p), None) == sp.EINVAL   # under 1 MiB
     assert L.splash_measure_peaks(0x1001, 1 << 30, ctypes.byref(p), None) == sp.EINVAL  # misaligned
     assert L.splash_measure_peaks(0x1000, 1 << 30, None, None) == sp.EINVAL
+
+
+def test_repack_binding_rejects_host_pools():
+    """A pool in host memory would hand a host pointer to the copy kernel: the
+    binding refuses it before anything reaches the library."""
+    import torch
+    src = torch.zeros((4, 2, 8), dtype=torch.int16)
+    dst = torch.zeros((4, 2, 8), dtype=torch.int16)
+    tab = torch.zeros((1, 4), dtype=torch.int32)
+    with pytest.raises(ValueError, match="src_pages must be on the GPU"):
+        sp.kv_repack(src, tab, dst, tab)
+
+
+def test_library_info_names_the_in_tree_build(splash):
+    info = sp.library_info()
+    assert info["path"] == os.path.join("layout_agnostic_latent_amd", "libsplash_attn.so")
+    assert len(info["sha256_16"]) == 16
+
+
+def test_splash_lib_outside_the_package_is_refused(tmp_path):
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, SPLASH_LIB=str(tmp_path / "libsplash_attn.so"), PYTHONPATH=root)
+    r = subprocess.run([sys.executable, "-c", "import layout_agnostic_latent_amd"], env=env, capture_output=True,
+                       text=True)
+    assert r.returncode != 0 and "outside the package directory" in r.stderr
+
