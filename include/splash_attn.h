@@ -125,6 +125,30 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
                        float* out, float* lse, hipStream_t stream);
 
 /*
+ * splash_decode_attn for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, semantics and kernels as splash_decode_attn,
+ * but the split-KV workspace is the library's static per-device scratch
+ * array of SPLASH_NOALLOC_SCRATCH_BYTES (64 MiB), which each GPU the
+ * library runs on holds until the process ends.  The call makes no
+ * hipMalloc / hipFree and no other allocating call, and records no
+ * profiling events.
+ *  - A share whose split-KV workspace (splash_decode_plan's
+ *    workspace_bytes) exceeds the scratch is rejected with SPLASH_EINVAL
+ *    before anything is launched.
+ *  - Every call on a GPU shares that GPU's scratch: calls that overlap on
+ *    one GPU (on different streams, or from different threads, while an
+ *    earlier call's kernels still run) race and give wrong results.  Calls
+ *    in one stream's order are safe.  Nothing in the scratch needs clearing
+ *    between calls (every value a merge reads is written by the same call).
+ */
+#define SPLASH_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+int splash_decode_attn_noalloc(const splash_desc* desc, const void* q, const void* kv_pages,
+                               const int32_t* block_table, const int32_t* seq_lens, int32_t head_lo,
+                               int32_t head_hi, int32_t tok_lo, int32_t tok_hi, float* out, float* lse,
+                               hipStream_t stream);
+
+/*
  * Merge n_parts partial results over disjoint token sets, per row:
  *   M = max_p lses[p][r] over finite entries
  *   lse_out[r] = M + log(sum_p exp(lses[p][r] - M))

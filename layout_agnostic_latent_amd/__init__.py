@@ -7,6 +7,7 @@ streams.  Import fails loudly if the library has not been built
 
 Functions mirror the C ABI in include/splash_attn.h:
   decode_attn(q, kv_pages, block_table, seq_lens, head_lo, head_hi, tok_lo, tok_hi, out, lse, ...)
+  decode_attn_noalloc(...)  (same arguments; split-KV workspace in a static scratch array)
   lse_merge(partials, lses, out, lse_out)
   kv_repack(src_pages, src_table, dst_pages, dst_table, err_count=None)
 """
@@ -16,7 +17,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["LIB_PATH", "SplashError", "lib", "library_info", "decode_attn", "decode_plan", "lse_merge", "kv_repack",
+__all__ = ["LIB_PATH", "SplashError", "lib", "library_info", "decode_attn", "decode_attn_noalloc", "decode_plan", "lse_merge", "kv_repack",
            "device_errors", "release_workspace", "profile_start", "profile_stop", "measure_peaks", "DEVERR_BAD_PAGE",
            "DEVERR_REPACK_PAIR", "DEVERR_PARTIAL_RANGE"]
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         i32, i64, vp, fp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
         L.splash_decode_attn.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, i32, i32, i32, i32, fp, fp, vp]
         L.splash_decode_attn.restype = ctypes.c_int
+        L.splash_decode_attn_noalloc.argtypes = L.splash_decode_attn.argtypes
+        L.splash_decode_attn_noalloc.restype = ctypes.c_int
         L.splash_lse_merge.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
         L.splash_lse_merge.restype = ctypes.c_int
         L.splash_kv_repack.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, vp]
@@ -155,6 +158,14 @@ def decode_attn(q, kv_pages, block_table, seq_lens, head_lo: int, head_hi: int, 
     lse fp32 [B, head_hi-head_lo] or None."""
     _decode("splash_decode_attn", q, kv_pages, block_table, seq_lens, head_lo, head_hi, tok_lo, tok_hi, out, lse,
             d_v, scale, num_splits, stream)
+
+
+def decode_attn_noalloc(q, kv_pages, block_table, seq_lens, head_lo: int, head_hi: int, tok_lo: int, tok_hi: int,
+                        out, lse=None, *, d_v: int, scale: float, num_splits: int = 0, stream=None) -> None:
+    """splash_decode_attn_noalloc: as decode_attn, with the split-KV workspace in the library's static
+    per-device scratch (no device allocation; overlapping calls on one GPU race)."""
+    _decode("splash_decode_attn_noalloc", q, kv_pages, block_table, seq_lens, head_lo, head_hi, tok_lo, tok_hi, out,
+            lse, d_v, scale, num_splits, stream)
 
 
 def _decode(entry, q, kv_pages, block_table, seq_lens, head_lo, head_hi, tok_lo, tok_hi, out, lse, d_v, scale,

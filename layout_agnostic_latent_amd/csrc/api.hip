@@ -61,9 +61,13 @@ hipEvent_t take_event() {
 
 // Runs `launch(start_event, stop_event)`; while profiling, the events are
 // attached to the kernel dispatch itself and kept for splash_profile_stop.
+// Profiling is skipped for calls that must not allocate (the event pool and
+// the launch list are host containers that may grow).
+thread_local bool t_no_alloc = false;
+
 template <typename F>
 hipError_t timed(int kind, F&& launch) {
-  if (!g_profiling) return launch(nullptr, nullptr);
+  if (!g_profiling || t_no_alloc) return launch(nullptr, nullptr);
   TimedLaunch t{kind, take_event(), take_event()};
   if (!t.start || !t.stop) return launch(nullptr, nullptr);
   hipError_t e = launch(t.start, t.stop);
@@ -106,6 +110,29 @@ int device_error_word(int dev, int32_t** out) {
   return SPLASH_OK;
 }
 
+// Scratch memory of splash_decode_attn_noalloc: the split-KV workspace of
+// callers that cannot allocate.  Each device holds its own copy for the life
+// of the process; host code reaches it only through the per-device address
+// from hipGetSymbolAddress (the array's name in host code is a host-side
+// stand-in, not a device address).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Caller holds g_mu.  Device address of `scratch` on `dev` (the current
+// device), looked up once per device.
+void* g_scratch[kMaxDevices] = {};
+int scratch_address(int dev, void** out) {
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(SPLASH_EHIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return SPLASH_OK;
+}
+
 // Caller holds g_mu.  The split-KV workspace of `stream` on `dev`, grown
 // (never shrunk) to at least `bytes`.  Growing frees the old buffer after
 // the stream's work on it is done, so it is refused while the stream is
@@ -127,7 +154,8 @@ int ensure_workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
     if (cs != hipStreamCaptureStatusNone)
       return fail(SPLASH_EINVAL,
                   "the split-KV workspace of this stream must grow to %zu bytes, which is not possible during "
-                  "stream capture: make one eager call of the same share on this stream first",
+                  "stream capture: make one eager call of the same share on this stream first, or use "
+                  "splash_decode_attn_noalloc",
                   bytes);
     if (w->ptr) {
       e = hipStreamSynchronize(stream);  // kernels in flight may still use the old buffer
@@ -354,9 +382,12 @@ namespace {
 
 // Decode attention of the share's heads [head_lo, head_hi): one decode
 // launch over every KV head the share touches (and one merge when split).
+// `fixed_ws` (with `fixed_ws_bytes`) is a workspace to use instead of the
+// stream's own, which is then never allocated or grown.
 int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, const int32_t* block_table,
                  const int32_t* seq_lens, int32_t head_lo, int32_t head_hi, int32_t tok_lo, int32_t tok_hi,
-                 float* out, float* lse, int dev, int32_t* dev_err, hipStream_t stream) {
+                 float* out, float* lse, int dev, int32_t* dev_err, hipStream_t stream, void* fixed_ws = nullptr,
+                 size_t fixed_ws_bytes = 0) {
   Plan p;
   int rc = make_plan(desc, head_lo, head_hi, tok_lo, tok_hi, &p);
   if (rc) return rc;
@@ -398,7 +429,14 @@ int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, con
   }
   // split-KV: partials in the workspace, then the merge writes the caller's rows
   void* ws;
-  if ((rc = ensure_workspace(dev, stream, (size_t)p.workspace_bytes, &ws))) return rc;
+  if (fixed_ws) {
+    if ((size_t)p.workspace_bytes > fixed_ws_bytes)
+      return fail(SPLASH_EINVAL, "this share needs %lld bytes of split-KV workspace, more than the %zu-byte scratch",
+                  (long long)p.workspace_bytes, fixed_ws_bytes);
+    ws = fixed_ws;
+  } else if ((rc = ensure_workspace(dev, stream, (size_t)p.workspace_bytes, &ws))) {
+    return rc;
+  }
   const int64_t rows = (int64_t)desc->num_reqs * hs;
   if (p.worklist) {
     const WorklistLayout w = worklist_layout(p.items_max, desc->num_reqs, hs, desc->d_v);
@@ -466,6 +504,35 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
   if ((rc = device_error_word(dev, &dev_err))) return rc;
   return decode_share(desc, q, (const uint16_t*)kv_pages, block_table, seq_lens, head_lo, head_hi, tok_lo, tok_hi,
                       out, lse, dev, dev_err, stream);
+}
+
+int splash_decode_attn_noalloc(const splash_desc* desc, const void* q, const void* kv_pages,
+                               const int32_t* block_table, const int32_t* seq_lens, int32_t head_lo,
+                               int32_t head_hi, int32_t tok_lo, int32_t tok_hi, float* out, float* lse,
+                               hipStream_t stream) {
+  Plan p;
+  int rc = make_plan(desc, head_lo, head_hi, tok_lo, tok_hi, &p);
+  if (rc) return rc;
+  if (!q || !kv_pages || !block_table || !seq_lens || !out)
+    return fail(SPLASH_EINVAL, "null tensor pointer (q, kv_pages, block_table, seq_lens and out are required)");
+  if ((((uintptr_t)q) & 15) || (((uintptr_t)kv_pages) & 15) || (((uintptr_t)out) & 15))
+    return fail(SPLASH_EINVAL, "q, kv_pages and out must be 16-byte aligned");
+  if ((size_t)p.workspace_bytes > kScratchBytes)
+    return fail(SPLASH_EINVAL, "this share needs %lld bytes of split-KV workspace, more than the %zu-byte scratch",
+                (long long)p.workspace_bytes, kScratchBytes);
+  if (desc->num_reqs == 0) return SPLASH_OK;
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  int32_t* dev_err;
+  if ((rc = device_error_word(dev, &dev_err))) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_address(dev, &ws))) return rc;
+  t_no_alloc = true;
+  rc = decode_share(desc, q, (const uint16_t*)kv_pages, block_table, seq_lens, head_lo, head_hi, tok_lo, tok_hi,
+                    out, lse, dev, dev_err, stream, ws, kScratchBytes);
+  t_no_alloc = false;
+  return rc;
 }
 
 int splash_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows, int32_t d_v,

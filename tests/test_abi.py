@@ -189,3 +189,14 @@ def test_splash_lib_outside_the_package_is_refused(tmp_path):
                        text=True)
     assert r.returncode != 0 and "outside the package directory" in r.stderr
 
+
+def test_noalloc_rejects_a_share_beyond_its_scratch(splash):
+    """A share whose split-KV workspace exceeds the static scratch is refused
+    on the host, before any HIP call."""
+    L = splash.lib()
+    # 64 forced chunks x 16 requests x 128 heads x 512 fp16 values = 128 MiB of partials
+    d = _desc(num_splits=64)
+    p = 0x1000
+    rc = L.splash_decode_attn_noalloc(ctypes.byref(d), p, p, p, p, 0, 128, 0, 4096, p, None, None)
+    assert rc == sp.EINVAL and b"scratch" in L.splash_last_error()
+    assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_splits=64)[2] > 64 << 20
