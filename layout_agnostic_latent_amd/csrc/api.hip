@@ -282,11 +282,11 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
     if (v == 32 || v == 64 || v == 128) wg_heads = v;
   }
   if (wg_heads == 32) {
-    p->variant = {d->d_qk, d->d_v, 1, wv_max};
+    p->variant = {d->d_qk, d->d_v, 1, wv_max, 0};
   } else if (wg_heads == 64 && d->d_v / 32 >= 2 && d->d_qk == 576) {
-    p->variant = {d->d_qk, d->d_v, 2, 2};
+    p->variant = {d->d_qk, d->d_v, 2, 2, 0};
   } else {
-    p->variant = {d->d_qk, d->d_v, 4, 1};
+    p->variant = {d->d_qk, d->d_v, 4, 1, 0};
   }
   p->heads_per_group = 32 * p->variant.wh;
   p->kv_group = group;
@@ -328,6 +328,10 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
     p->grid_splits = max_tiles > 0 ? (int)((max_tiles + chunk - 1) / chunk) : 1;
   }
   if (p->grid_splits < 1) p->grid_splits = 1;
+  // Longest chunk (in tiles) any workgroup can get: forced splits cut each
+  // request's tiles evenly, every other plan caps chunks at kMaxChunkTiles.
+  p->variant.max_chunk_tiles = forced > 0 ? (max_tiles + forced - 1) / forced
+                                          : (max_tiles < kMaxChunkTiles ? max_tiles : kMaxChunkTiles);
   if (p->grid_splits > 65535) return fail(SPLASH_EINVAL, "too many split-KV chunks (%d)", p->grid_splits);
   p->worklist = false;
   p->items_max = 0;

@@ -62,9 +62,12 @@ struct DecodeArgs {
 };
 
 // Kernel variants: (d_qk, d_v) with WH waves along the heads (32 heads each)
-// and WV waves along the V columns.
+// and WV waves along the V columns; max_chunk_tiles bounds the 32-token
+// tiles any one workgroup of the launch processes (it selects how the DMA
+// addresses are kept).
 struct DecodeVariant {
   int d_qk, d_v, wh, wv;
+  int64_t max_chunk_tiles;
 };
 
 // Records `msg` as the thread's last error (splash_last_error) and returns

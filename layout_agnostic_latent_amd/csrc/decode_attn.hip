@@ -62,6 +62,10 @@ constexpr int kMaxBuf = 4;
 constexpr float kHalfMax = 65504.0f;  // largest finite fp16 (split-KV partials are stored in fp16)
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = exp2(s - m) stays <= 256
 constexpr int kPlanStep = 22;  // PV MFMA after which the next tile's DMA plan is made (past the max slices)
+constexpr int kTblLoadStep = 12;  // PV MFMA after which the table entry of that plan is read
+// Tiles per chunk the tile-address table holds (four waves x 8 bytes each: the
+// 16 KiB page-id area of the four-wave, 32-head-per-wave variant).
+constexpr int kTblTiles = 512;
 
 // LDS tile layout ("slabs"): the 16-byte chunk c of tile row r lives at
 //   (c / 8) * SLAB_B + r * 128 + ((c % 8) ^ row_swizzle(r)) * 16,
@@ -83,6 +87,17 @@ __device__ __forceinline__ uint32_t row_swizzle(uint32_t row) {
 __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)),
                "v"(voff), "s"(sbase)
+               : "memory");
+}
+
+// The same copy for instruction I of a wave's row group, `lds_addr` being
+// that instruction's LDS destination: the 128-byte step between the
+// instructions' global addresses is the immediate offset, which the
+// hardware adds to the LDS address too, so m0 is lowered by it.
+template <int I>
+__device__ __forceinline__ void lds_dma16_imm(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3 nt" ::"{m0}"(lds_addr - 128 * I), "v"(voff),
+               "s"(sbase), "n"(128 * I)
                : "memory");
 }
 
@@ -379,9 +394,15 @@ struct Cfg {
   static_assert(VB % PB == 0, "epilogue passes");
 };
 
-template <int D_QK, int D_V, int WH, int WV>
+// TBL: DMA addresses from a per-wave table of tile addresses built in the
+// prologue (four waves, one row group each, no slab padding, chunks of at
+// most kTblTiles tiles); otherwise from page ids looked up per tile.
+template <int D_QK, int D_V, int WH, int WV, bool TBL>
 __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const DecodeArgs a) {
   using C = Cfg<D_QK, D_V, WH, WV>;
+  static_assert(!TBL || (C::NW == 4 && !C::PADDED && !C::KSPLIT && C::DMA_W <= 9 &&
+                         C::BODY_B + 4 * kTblTiles * 8 <= C::SMEM_B),
+                "tile-address table layout");
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_B];
   // this chunk's physical page ids; with the split score contraction only
   // the plan's scratch, in the (then unused) exchange area
@@ -569,6 +590,22 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     return d;
   };
   auto issue_one = [&](const DmaPlan& d, int i) {
+    if constexpr (TBL) {
+      // one 64-bit base for the wave's nine instructions (immediate offsets);
+      // instruction i fills slab i of the wave's rows, at d.lds + i * SLAB_B
+      switch (i) {
+        case 0: lds_dma16_imm<0>(d.wbase, d.voff, d.lds + 0 * C::SLAB_B); break;
+        case 1: lds_dma16_imm<1>(d.wbase, d.voff, d.lds + 1 * C::SLAB_B); break;
+        case 2: lds_dma16_imm<2>(d.wbase, d.voff, d.lds + 2 * C::SLAB_B); break;
+        case 3: lds_dma16_imm<3>(d.wbase, d.voff, d.lds + 3 * C::SLAB_B); break;
+        case 4: lds_dma16_imm<4>(d.wbase, d.voff, d.lds + 4 * C::SLAB_B); break;
+        case 5: lds_dma16_imm<5>(d.wbase, d.voff, d.lds + 5 * C::SLAB_B); break;
+        case 6: lds_dma16_imm<6>(d.wbase, d.voff, d.lds + 6 * C::SLAB_B); break;
+        case 7: lds_dma16_imm<7>(d.wbase, d.voff, d.lds + 7 * C::SLAB_B); break;
+        default: lds_dma16_imm<8>(d.wbase, d.voff, d.lds + 8 * C::SLAB_B); break;
+      }
+      return;
+    }
     if constexpr (C::NW == 4 && !C::PADDED) {
       lds_dma16_s(d.wbase + 128 * i, d.voff, d.lds + (4 * i + wave) * 1024);
       return;
@@ -580,6 +617,31 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     if (C::PADDED && chunk >= C::NCH) chunk = 0;  // slab padding: any in-row chunk
     const char* base = (one_page_per_tile || min(max(R, d.rlo), d.rhi1) < 16) ? d.base0 : d.base1;
     lds_dma16_s(base, (uint32_t)(row * row_b + chunk * 16), d.lds + nn * 1024);
+  };
+
+  // Tile-address table (TBL): entry [w][i] is the pool address of the first
+  // row of wave w's row group in tile i of the chunk, i.e. of token
+  // clamp(32 (t_begin + i) + 8w, mlo, mhi - 1); the group's other rows are
+  // at most 7 rows further on the same page.  The lane offset is the same
+  // for every interior tile; the first and last tiles clamp rows outside
+  // [mlo, mhi) to the nearest valid row of the group.
+  uint64_t* const tbl = (uint64_t*)(smem + C::BODY_B) + (TBL ? wave * kTblTiles : 0);
+  const uint32_t chunk_off = 16u * ((uint32_t)(lane & 7) ^ row_swizzle(8 * wave + l8));
+  const uint32_t voff_int = (uint32_t)(l8 * row_b) + chunk_off;
+  auto tbl_plan = [&](uint64_t entry, int i, int slot) -> DmaPlan {
+    DmaPlan d{};
+    const uint32_t lo32 = __builtin_amdgcn_readfirstlane((uint32_t)entry);
+    const uint32_t hi32 = __builtin_amdgcn_readfirstlane((uint32_t)(entry >> 32));
+    d.wbase = (const char*)(uintptr_t)(((uint64_t)hi32 << 32) | lo32);
+    d.lds = smem_base + slot * C::TILE_B + wave * 1024;
+    d.voff = voff_int;
+    if (i == 0 || i == ntiles - 1) {
+      const int tokg = (t_begin + i) * kTileTok + 8 * wave;
+      const int tokw = min(max(tokg, mlo), mhi - 1);
+      const int row = min(max(tokg + l8, mlo), mhi - 1);
+      d.voff = (uint32_t)((row - tokw) * row_b) + chunk_off;
+    }
+    return d;
   };
 
   // ---- online-softmax state (per head = per lane column) ----
@@ -838,7 +900,9 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // new max if it moved (lazily: only when it grew by more than 2^8).
   auto pv_and_max = [&](int it, floatx16& s, const bf16x8 (&pcur)[2], bf16x8 (&vring)[PV_PF], auto with_dma,
                         const DmaPlan& dp, auto&& extra) {
-    mask_tile(s, it);
+    // tiles of the main loop (with_dma) lie strictly inside the chunk: only
+    // the first and the last tile can hold rows outside [mlo, mhi)
+    if constexpr (!decltype(with_dma)::value) mask_tile(s, it);
     float mx[4];
     float m_new = m_run;
     const float thr = m_run + kRescaleThreshold;
@@ -929,7 +993,22 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // the two share.  Up to 64 * kVPages pages go to VGPRs, up to kPageLds to
   // LDS; longer chunks read the table through the scalar cache.
   const int32_t* bt_src = a.bt + (int64_t)b * a.max_pages + j0;
-  if (pt_vgpr) {
+  // TBL: this wave's block-table entries, one per tile (lane i % 64 of
+  // register i / 64), loaded before Q; the table is built once they land.
+  constexpr int kTblRegs = TBL ? kTblTiles / 64 : 1;
+  int32_t tpg[kTblRegs];
+  if constexpr (TBL) {
+    const int32_t* bt_b = a.bt + (int64_t)b * a.max_pages;
+#pragma unroll
+    for (int k = 0; k < kTblRegs; ++k) {
+      tpg[k] = 0;
+      if (k * 64 < ntiles) {
+        const int i = min(k * 64 + lane, ntiles - 1);
+        const int tokw = min(max((t_begin + i) * kTileTok + 8 * wave, mlo), mhi - 1);
+        tpg[k] = bt_b[tokw >> a.page_shift];
+      }
+    }
+  } else if (pt_vgpr) {
 #pragma unroll
     for (int k = 0; k < kVPages; ++k) vpg[k] = j0 + 64 * k + lane <= j1 ? bt_src[64 * k + lane] : 0;
   } else if (pt_lds) {
@@ -950,7 +1029,27 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     }
   }
   asm volatile("" ::: "memory");
-  if (pt_vgpr) {
+  if constexpr (TBL) {
+    // The table (the compiler waits for the entries, not for the younger Q
+    // loads).  An entry outside the pool is read as page 0 and flagged.
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < kTblRegs; ++k) {
+      if (k * 64 < ntiles) {
+        const int i = k * 64 + lane;
+        const int tokw = min(max((t_begin + min(i, ntiles - 1)) * kTileTok + 8 * wave, mlo), mhi - 1);
+        uint32_t pg = (uint32_t)tpg[k];
+        if (i < ntiles && pg >= (uint32_t)a.num_pages) {
+          bad = true;
+          pg = 0;
+        }
+        const uint64_t addr = (uint64_t)(uintptr_t)kv + (uint64_t)pg * (uint64_t)(a.page_stride * 2) +
+                              (uint64_t)((tokw & ps_mask) * row_b);
+        if (i < ntiles) tbl[i] = addr;
+      }
+    }
+    if (__any(bad)) bad_page = true;
+  } else if (pt_vgpr) {
     // the page ids are complete here (the compiler waits for them, not for
     // the younger Q loads), so the loop never waits on them
 #pragma unroll
@@ -963,7 +1062,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     if (i < ntiles) {
-      const DmaPlan d = dma_plan(t_begin + i, i, pages_of(t_begin + i));
+      const DmaPlan d = TBL ? tbl_plan(tbl[i], i, i) : dma_plan(t_begin + i, i, pages_of(t_begin + i));
 #pragma unroll
       for (int k = 0; k < C::DMA_W; ++k) issue_one(d, k);
     }
@@ -977,7 +1076,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     if (ntiles > 1) wait_vmcnt<C::DMA_W>();
     else wait_vmcnt<0>();
     __syncthreads();
-    dp = dma_plan(t_begin + 2, 2 % C::NBUF, pages_of(t_begin + min(2, ntiles - 1)));
+    dp = TBL ? tbl_plan(tbl[min(2, ntiles - 1)], 2, 2 % C::NBUF)
+             : dma_plan(t_begin + 2, 2 % C::NBUF, pages_of(t_begin + min(2, ntiles - 1)));
     // The compiler waits for each Q operand at its MFMA, counting only its
     // own loads: with tile 1's DMA younger than Q, the last of those waits
     // also drain tile 1.  Tile 2's DMA is therefore issued after the scores,
@@ -990,7 +1090,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     mask_tile(s, 0);
     m_run = tile_max(s);
     sprev = s;
-    if (3 < ntiles) dp = dma_plan(t_begin + 3, 3 % C::NBUF, pages_of(t_begin + 3));
+    if (3 < ntiles) dp = TBL ? tbl_plan(tbl[3], 3, 3 % C::NBUF) : dma_plan(t_begin + 3, 3 % C::NBUF, pages_of(t_begin + 3));
   }
 
   // Main loop, iteration j: wait for tile j and barrier (every wave is done
@@ -1009,8 +1109,14 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     floatx16 s = qk_and_exp(it, kDma, true, dp, vring, sprev, pcur);
     DmaPlan dp_next = dp;
     const int tn = t_begin + it + 3;
+    uint64_t entry = 0;  // table entry of tile it + 3 (TBL), read early, used at the plan step
     pv_and_max(it, s, pcur, vring, kDma, dp, [&](int i) {
-      if (i == kPlanStep && tn < t_end) dp_next = dma_plan(tn, (it + 3) % C::NBUF, pages_of(tn));
+      if constexpr (TBL) {
+        if (i == kTblLoadStep && tn < t_end) entry = tbl[it + 3];
+        if (i == kPlanStep && tn < t_end) dp_next = tbl_plan(entry, it + 3, (it + 3) % C::NBUF);
+      } else {
+        if (i == kPlanStep && tn < t_end) dp_next = dma_plan(tn, (it + 3) % C::NBUF, pages_of(tn));
+      }
     });
     sprev = s;
     dp = dp_next;
@@ -1106,9 +1212,10 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     *lse_ptr = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
 }
 
-template <int D_QK, int D_V, int WH, int WV>
+template <int D_QK, int D_V, int WH, int WV, bool TBL = false>
 hipError_t launch_variant(dim3 grid, const DecodeArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
-  hipExtLaunchKernelGGL((decode_attn_kernel<D_QK, D_V, WH, WV>), grid, dim3(64 * WH * WV), 0, stream, e0, e1, 0, a);
+  hipExtLaunchKernelGGL((decode_attn_kernel<D_QK, D_V, WH, WV, TBL>), grid, dim3(64 * WH * WV), 0, stream, e0, e1, 0,
+                        a);
   return hipGetLastError();
 }
 
@@ -1117,7 +1224,10 @@ hipError_t launch_variant(dim3 grid, const DecodeArgs& a, hipStream_t stream, hi
 hipError_t launch_decode(const DecodeVariant& v, dim3 grid, const DecodeArgs& a, hipStream_t stream, hipEvent_t e0,
                          hipEvent_t e1) {
   if (v.d_qk == 576 && v.d_v == 512) {
-    if (v.wh == 4 && v.wv == 1) return launch_variant<576, 512, 4, 1>(grid, a, stream, e0, e1);
+    if (v.wh == 4 && v.wv == 1) {
+      if (v.max_chunk_tiles <= kTblTiles) return launch_variant<576, 512, 4, 1, true>(grid, a, stream, e0, e1);
+      return launch_variant<576, 512, 4, 1>(grid, a, stream, e0, e1);
+    }
     if (v.wh == 2 && v.wv == 2) return launch_variant<576, 512, 2, 2>(grid, a, stream, e0, e1);
     if (v.wh == 1 && v.wv == 4) return launch_variant<576, 512, 1, 4>(grid, a, stream, e0, e1);
   }
