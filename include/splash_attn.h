@@ -129,7 +129,7 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, semantics and kernels as splash_decode_attn,
  * but the split-KV workspace is the library's static per-device scratch
- * array of SPLASH_NOALLOC_SCRATCH_BYTES (64 MiB), which each GPU the
+ * array of SPLASH_NOALLOC_SCRATCH_BYTES (72 MiB), which each GPU the
  * library runs on holds until the process ends.  The call makes no
  * hipMalloc / hipFree and no other allocating call, and records no
  * profiling events.
@@ -142,7 +142,7 @@ int splash_decode_attn(const splash_desc* desc, const void* q, const void* kv_pa
  *    in one stream's order are safe.  Nothing in the scratch needs clearing
  *    between calls (every value a merge reads is written by the same call).
  */
-#define SPLASH_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+#define SPLASH_NOALLOC_SCRATCH_BYTES ((int64_t)72 << 20)
 int splash_decode_attn_noalloc(const splash_desc* desc, const void* q, const void* kv_pages,
                                const int32_t* block_table, const int32_t* seq_lens, int32_t head_lo,
                                int32_t head_hi, int32_t tok_lo, int32_t tok_hi, float* out, float* lse,

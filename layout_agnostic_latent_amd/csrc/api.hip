@@ -115,7 +115,7 @@ int device_error_word(int dev, int32_t** out) {
 // of the process; host code reaches it only through the per-device address
 // from hipGetSymbolAddress (the array's name in host code is a host-side
 // stand-in, not a device address).
-constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr size_t kScratchBytes = (size_t)72 << 20;
 static __device__ __align__(256) char scratch[kScratchBytes];
 
 // Caller holds g_mu.  Device address of `scratch` on `dev` (the current
@@ -190,44 +190,47 @@ struct Plan {
   int kv_group;         // query heads per KV head
   int kv_first;         // first KV head the share touches
   int z_per_kv;         // head groups per KV head
-  int grid_splits;      // blockIdx.x extent
+  int grid_splits;      // split-KV chunks per request (grid mode: the blockIdx.x extent)
   int fixed_splits;     // > 0: every request cut into this many chunks
   int chunk_tiles;      // otherwise: 32-token tiles per chunk
-  // Work-list mode: the decode kernel cuts the chunks from the real lengths;
-  // at most items_max work items (the grid's x extent).
-  bool worklist;
-  int items_max;
-  int target;           // workgroups per head group the chunk length aims at
+  // Stream mode: the decode kernel cuts the batch's tiles into at most
+  // `target` equal ranges per head group (the grid's x extent) from the real
+  // lengths; each range leaves at most two partials.
+  bool stream;
+  int target;
+  int header;           // tiles a segment start is counted as in the device plan
   int64_t workspace_bytes;
 };
 
-// Work-list workspace layout (byte offsets; every part 256-byte aligned):
-// partial outputs (fp16) and LSEs (fp32) per work item, then each request's
-// part list.
-struct WorklistLayout {
+// The fixed cost of starting a segment (Q loads, pipeline fill and drain,
+// the epilogue) in units of one tile of the variant's loop.  Measured on
+// MI355X for 128-head groups by the decode time of the 64-request
+// transition batch against the header: 0 / 3 / 5 / 8 / 12 / 16 tiles gave
+// 242 / 237 / 236 / 232 / 226 / 230 us (best of five).  Narrower head
+// groups have cheaper tiles, so the same start counts as more of them.
+constexpr int kMinRangeTiles = 4;
+int segment_header_tiles(int heads_per_group) {
+  if (const char* env = getenv("SPLASH_PLAN_HEADER")) {
+    const int v = atoi(env);
+    if (v >= 0 && v <= 64) return v;
+  }
+  return heads_per_group >= 128 ? 12 : (heads_per_group >= 64 ? 20 : 32);
+}
+
+// Split-KV workspace layout (byte offsets; every part 256-byte aligned):
+// `parts` partial rows of fp16 outputs, their {LSE, scale} records (one per
+// column group), then (in stream mode) each request's merge record.
+struct PartLayout {
   int64_t part_o, part_l, req_info, total;
 };
 int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
-WorklistLayout worklist_layout(int64_t items, int64_t B, int64_t hs, int64_t d_v) {
-  WorklistLayout w;
+PartLayout part_layout(int64_t parts, int64_t d_v, int64_t groups, int64_t records) {
+  PartLayout w;
   w.part_o = 0;
-  w.part_l = align256(w.part_o + items * hs * d_v * (int64_t)sizeof(uint16_t));
-  w.req_info = align256(w.part_l + items * hs * (int64_t)sizeof(float));
-  w.total = align256(w.req_info + B * 16);
+  w.part_l = align256(w.part_o + parts * d_v * (int64_t)sizeof(uint16_t));
+  w.req_info = align256(w.part_l + parts * groups * 8);
+  w.total = align256(w.req_info + records * 16);
   return w;
-}
-
-// Grid-mode workspace: fp16 partial outputs [splits][rows][d_v], then fp32
-// LSEs [splits][rows].
-struct GridLayout {
-  int64_t part_o, part_l, total;
-};
-GridLayout grid_layout(int64_t splits, int64_t rows, int64_t d_v) {
-  GridLayout g;
-  g.part_o = 0;
-  g.part_l = align256(splits * rows * d_v * (int64_t)sizeof(uint16_t));
-  g.total = align256(g.part_l + splits * rows * (int64_t)sizeof(float));
-  return g;
 }
 
 // Latent KV heads of the pool (0 in the descriptor means one).
@@ -328,30 +331,39 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
     p->grid_splits = max_tiles > 0 ? (int)((max_tiles + chunk - 1) / chunk) : 1;
   }
   if (p->grid_splits < 1) p->grid_splits = 1;
-  // Longest chunk (in tiles) any workgroup can get: forced splits cut each
-  // request's tiles evenly, every other plan caps chunks at kMaxChunkTiles.
+  if (p->grid_splits > 65535) return fail(SPLASH_EINVAL, "too many split-KV chunks (%d)", p->grid_splits);
+  p->stream = false;
+  p->target = 0;
+  p->header = 0;
+  // Longest run of tiles any one workgroup gets: forced splits cut each
+  // request's tiles evenly, grid chunks are at most kMaxChunkTiles.
   p->variant.max_chunk_tiles = forced > 0 ? (max_tiles + forced - 1) / forced
                                           : (max_tiles < kMaxChunkTiles ? max_tiles : kMaxChunkTiles);
-  if (p->grid_splits > 65535) return fail(SPLASH_EINVAL, "too many split-KV chunks (%d)", p->grid_splits);
-  p->worklist = false;
-  p->items_max = 0;
-  p->target = 0;
+  const int64_t rows = (int64_t)d->num_reqs * hs;
+  const int64_t groups = d->d_v / partial_group_cols(d->d_v, p->variant.wv);
   if (p->grid_splits == 1) {
     p->workspace_bytes = 0;
   } else if (forced > 0 || d->num_reqs > kPlanMaxReqs) {
-    p->workspace_bytes = grid_layout(p->grid_splits, (int64_t)d->num_reqs * hs, d->d_v).total;
+    p->workspace_bytes = part_layout((int64_t)p->grid_splits * rows, d->d_v, groups, 0).total;
   } else {
     // Requests may be shorter than the table's capacity (ragged batches):
-    // the kernel cuts the chunks from seq_lens.  Full chunks number
-    // at most max(target, B * max_tiles / kMaxChunkTiles), plus one
-    // remainder chunk per request.
-    p->worklist = true;
+    // the kernel cuts the batch's tiles (each request's run counted with a
+    // header of `header` tiles for the cost of a segment start) into at
+    // most `target` equal ranges per head group, of at least kMinRangeTiles
+    // tiles, each leaving at most two partials; a range holds at most
+    // ceil(B * (max_tiles + header) / target) + 1 tiles.  The device plan is
+    // 32-bit, so longer batches take the grid plan.
+    p->header = segment_header_tiles(p->heads_per_group);
+    const int64_t tv_max = (int64_t)d->num_reqs * (max_tiles + p->header);
     p->target = (int)((kNumCUs + p->head_groups - 1) / p->head_groups);
-    const int64_t by_cap = (int64_t)d->num_reqs * max_tiles / kMaxChunkTiles;
-    const int64_t items = (by_cap > p->target ? by_cap : p->target) + d->num_reqs;
-    if (items > 65535) return fail(SPLASH_EINVAL, "too many split-KV work items (%lld)", (long long)items);
-    p->items_max = (int)items;
-    p->workspace_bytes = worklist_layout(items, d->num_reqs, hs, d->d_v).total;
+    if (tv_max >= ((int64_t)1 << 31)) {
+      p->workspace_bytes = part_layout((int64_t)p->grid_splits * rows, d->d_v, groups, 0).total;
+      return SPLASH_OK;
+    }
+    p->stream = true;
+    const int64_t per = (tv_max + p->target - 1) / p->target + 1;
+    p->variant.max_chunk_tiles = per > kMinRangeTiles + 1 ? per : kMinRangeTiles + 1;
+    p->workspace_bytes = part_layout(2 * (int64_t)p->target * hs, d->d_v, groups, d->num_reqs).total;
   }
   return SPLASH_OK;
 }
@@ -416,17 +428,15 @@ int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, con
   a.n_heads = hs;
   a.tok_lo = tok_lo;
   a.tok_hi = tok_hi;
+  a.num_reqs = desc->num_reqs;
   a.fixed_splits = p.fixed_splits;
   a.chunk_tiles = p.chunk_tiles;
   a.scale_log2 = desc->scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
 
-  const dim3 grid(p.grid_splits, desc->num_reqs, p.head_groups);
+  const dim3 grid(p.stream ? p.target : p.grid_splits, p.stream ? 1 : desc->num_reqs, p.head_groups);
   if (p.grid_splits == 1) {
-    a.out = out;
-    a.lse = lse;
-    a.out_split_stride = 0;
-    a.lse_split_stride = 0;
-    a.partial_out = 0;
     hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
     if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
     return SPLASH_OK;
@@ -442,44 +452,29 @@ int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, con
     return rc;
   }
   const int64_t rows = (int64_t)desc->num_reqs * hs;
-  if (p.worklist) {
-    const WorklistLayout w = worklist_layout(p.items_max, desc->num_reqs, hs, desc->d_v);
-    char* base = (char*)ws;
-    uint16_t* part_o = (uint16_t*)(base + w.part_o);
-    float* part_l = (float*)(base + w.part_l);
-    int4* req_info = (int4*)(base + w.req_info);
-    a.num_reqs = desc->num_reqs;
+  const int gcols = partial_group_cols(desc->d_v, p.variant.wv);
+  const int64_t groups = desc->d_v / gcols;
+  const PartLayout w = p.stream ? part_layout(2 * (int64_t)p.target * hs, desc->d_v, groups, desc->num_reqs)
+                                : part_layout((int64_t)p.grid_splits * rows, desc->d_v, groups, 0);
+  const int sc_shift = __builtin_ctz((unsigned)gcols);
+  char* base = (char*)ws;
+  a.part_o = (uint16_t*)(base + w.part_o);
+  a.part_l = (float*)(base + w.part_l);
+  if (p.stream) {
+    a.req_info = (int4*)(base + w.req_info);
     a.plan_target = p.target;
-    a.plan_min_chunk = 4;
-    a.plan_max_chunk = kMaxChunkTiles;
-    a.req_info = req_info;
-    a.out = (float*)part_o;  // fp16 partials (partial_out = 1)
-    a.lse = part_l;
-    a.out_split_stride = (int64_t)hs * desc->d_v;
-    a.lse_split_stride = hs;
-    a.partial_out = 1;
-    const dim3 wgrid(p.items_max, 1, p.head_groups);
-    hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, wgrid, a, stream, e0, e1); });
-    if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
-    e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
-      return launch_split_merge_segmented(part_o, part_l, req_info, (int32_t)rows, hs, desc->d_v, out, lse, stream,
-                                          e0, e1);
-    });
-    if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
-    return SPLASH_OK;
+    a.plan_min_chunk = kMinRangeTiles;
+    a.plan_header = p.header;
+  } else {
+    a.grid_partial = 1;
   }
-  const GridLayout gl = grid_layout(p.grid_splits, rows, desc->d_v);
-  uint16_t* part_o = (uint16_t*)((char*)ws + gl.part_o);
-  float* part_l = (float*)((char*)ws + gl.part_l);
-  a.out = (float*)part_o;  // fp16 partials (partial_out = 1)
-  a.lse = part_l;
-  a.out_split_stride = rows * desc->d_v;
-  a.lse_split_stride = rows;
-  a.partial_out = 1;
   hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
   if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
   e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
-    return launch_split_merge(part_o, part_l, p.grid_splits, (int32_t)rows, desc->d_v, out, lse, stream, e0, e1);
+    return p.stream ? launch_split_merge_stream(a.part_o, a.part_l, sc_shift, a.req_info, (int32_t)rows, hs,
+                                                desc->d_v, out, lse, stream, e0, e1)
+                    : launch_split_merge(a.part_o, a.part_l, sc_shift, p.grid_splits, (int32_t)rows, desc->d_v,
+                                         out, lse, stream, e0, e1);
   });
   if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
   return SPLASH_OK;

@@ -38,6 +38,7 @@
 // Attention with Seamless Handoff for LLM Serving" (weekinpapers.com); the
 // thelatestinai page is that paper's summary with its appendix tables
 // (thelatestinai.com).
+#include <climits>
 #include <type_traits>
 
 #include "common.h"
@@ -63,9 +64,9 @@ constexpr float kHalfMax = 65504.0f;  // largest finite fp16 (split-KV partials 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = exp2(s - m) stays <= 256
 constexpr int kPlanStep = 22;  // PV MFMA after which the next tile's DMA plan is made (past the max slices)
 constexpr int kTblLoadStep = 12;  // PV MFMA after which the table entry of that plan is read
-// Tiles per chunk the tile-address table holds (four waves x 8 bytes each: the
-// 16 KiB page-id area of the four-wave, 32-head-per-wave variant).
-constexpr int kTblTiles = 512;
+// Tiles per segment the tile-address table holds (four waves x 4 bytes each:
+// the 16 KiB page-id area of the four-wave, 32-head-per-wave variant).
+constexpr int kTblTiles = 1024;
 
 // LDS tile layout ("slabs"): the 16-byte chunk c of tile row r lives at
 //   (c / 8) * SLAB_B + r * 128 + ((c % 8) ^ row_swizzle(r)) * 16,
@@ -149,206 +150,175 @@ __device__ __forceinline__ void mfma_vgpr_last(floatx16& c, const bf16x8& a, con
                : "v"(a), "v"(b));
 }
 
-// Work-list plan, computed by every workgroup from the device's seq_lens
-// (the host knows only the block table's capacity, which for a ragged batch
-// says little about the work).  Chunk length: the batch's total tiles over
-// plan_target workgroups, clamped to [plan_min_chunk, plan_max_chunk].
-// Items: every request's full chunks, numbered in request order, then one
-// remainder chunk per request that has one.  Returns {request, first tile,
-// end tile, item} for item blockIdx.x, or request -1 past the last item.
-// `scratch` (LDS, >= 64 ints) is free again on return.
-template <int NT>
-__device__ int4 plan_item(const DecodeArgs& a, int32_t* scratch) {
-  constexpr int NWV = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lo = max(a.tok_lo, 0);
-  const int first = lo / kTileTok;
-  const int cap = a.max_pages << a.page_shift;
-  const int per = (a.num_reqs + NT - 1) / NT;  // requests per thread: [tid*per, tid*per + per)
-  auto tiles = [&](int r) -> int {
-    const int h = min(min(a.tok_hi, a.seq_lens[r]), cap);
-    return h > lo ? (h + kTileTok - 1) / kTileTok - first : 0;
-  };
-  // Each pass below visits this thread's requests: f(r, tiles of r).  With
-  // one request per thread (batches of up to NT requests) its tiles are
-  // loaded once, into a register; re-reading seq_lens after each barrier
-  // would put a dependent memory round trip into every pass.
-  const bool cached = per == 1;
-  const int tcache = (cached && tid < a.num_reqs) ? tiles(tid) : 0;
-  auto tiles_k = [&](int r) -> int { return cached ? tcache : tiles(r); };  // r = tid * per + k
-  long long mine = 0;
-  for (int k = 0; k < per; ++k) {
-    const int r = tid * per + k;
-    if (r < a.num_reqs) mine += tiles_k(r);
-  }
-  for (int d = 32; d >= 1; d >>= 1) mine += __shfl_xor(mine, d, 64);
-  long long* red = (long long*)scratch;  // [NWV]
-  if (lane == 0) red[wave] = mine;
-  __syncthreads();
-  long long total = 0;
-  for (int w = 0; w < NWV; ++w) total += red[w];
-  const long long full_cap = (long long)a.plan_target * a.plan_max_chunk;
-  int chunk = total >= full_cap ? a.plan_max_chunk
-                                : max(a.plan_min_chunk, ((int)total + a.plan_target - 1) / a.plan_target);
-  // Per thread: full chunks nf and remainder chunks nr of its requests at
-  // chunk length c; their inclusive prefix over the wave (fi, ri), the
-  // prefix before this wave (fb, rb) and the totals (F, R).  wsum: LDS,
-  // [NWV][2], clear of red[].
-  int* wsum = scratch + 2 * NWV + 8;
-  int* mine_item = scratch + 4 * NWV + 16;  // [4]: this workgroup's item
-  if (tid == 0) mine_item[0] = -1;          // ordered by the barrier below
-  int nf = 0, nr = 0, fi = 0, ri = 0, fb = 0, rb = 0, F = 0, R = 0;
-  auto count_items = [&](int c) {
-    nf = 0;
-    nr = 0;
-    for (int k = 0; k < per; ++k) {
-      const int r = tid * per + k;
-      if (r < a.num_reqs) {
-        const int nt = tiles_k(r);
-        nf += nt / c;
-        nr += (nt % c) ? 1 : 0;
-      }
-    }
-    fi = nf;
-    ri = nr;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int uf = __shfl_up(fi, d, 64), ur = __shfl_up(ri, d, 64);
-      if (lane >= d) {
-        fi += uf;
-        ri += ur;
-      }
-    }
-    if (lane == 63) {
-      wsum[2 * wave] = fi;
-      wsum[2 * wave + 1] = ri;
-    }
-    __syncthreads();
-    fb = rb = F = R = 0;
-    for (int w = 0; w < NWV; ++w) {
-      if (w < wave) {
-        fb += wsum[2 * w];
-        rb += wsum[2 * w + 1];
-      }
-      F += wsum[2 * w];
-      R += wsum[2 * w + 1];
-    }
-  };
-  count_items(chunk);
-  // A ragged batch's remainder chunks can overflow one round of plan_target
-  // workgroups (F + R items); the items past it then start only when earlier
-  // ones end, which can double the critical path.  Take the shortest chunk
-  // that fits one round instead, if any chunk up to the maximum does.  Items
-  // at length c are the sum over requests of ceil(tiles / c), a block-wide
-  // count; uniform batches fit at the first length and never count again.
-  if (F + R > a.plan_target && chunk < a.plan_max_chunk) {
-    auto items_at = [&](int c) -> int {
-      __syncthreads();  // every thread has read wsum before it is rewritten
-      count_items(c);
-      return F + R;
-    };
-    if (items_at(a.plan_max_chunk) <= a.plan_target) {
-      int lo = chunk, hi = a.plan_max_chunk;  // items_at(lo) > target >= items_at(hi)
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (items_at(mid) <= a.plan_target) hi = mid;
-        else lo = mid;
-      }
-      chunk = hi;
-    }
-    __syncthreads();
-    count_items(chunk);
-  }
-  int foff = fb + fi - nf;
-  int rnext = F + rb + ri - nr;
-  const int me = blockIdx.x;
-  const bool writer = blockIdx.x == 0 && blockIdx.z == 0;
-  for (int k = 0; k < per; ++k) {  // in request order: foff and rnext accumulate
-    const int r = tid * per + k;
-    if (r >= a.num_reqs) break;
-    const int nt = tiles_k(r);
-    const int nfull = nt / chunk;
-    const int rslot = (nt % chunk) ? rnext++ : -1;
-    if (me >= foff && me < foff + nfull) {
-      const int t0 = first + (me - foff) * chunk;
-      mine_item[0] = r;
-      mine_item[1] = t0;
-      mine_item[2] = t0 + chunk;
-    } else if (me == rslot) {
-      mine_item[0] = r;
-      mine_item[1] = first + nfull * chunk;
-      mine_item[2] = first + nt;
-    }
-    if (writer) a.req_info[r] = make_int4(foff, nfull, rslot, 0);
-    foff += nfull;
-  }
-  __syncthreads();
-  const int4 it = make_int4(mine_item[0], mine_item[1], mine_item[2], me);
-  __syncthreads();
-  return it;
+// Balanced split-KV plan, computed by every workgroup from the device's
+// seq_lens (the host knows only the block table's capacity, which for a
+// ragged batch says little about the work).  Every request with work
+// occupies a run of "virtual" tiles: a header of plan_header tiles (the
+// fixed cost of starting a segment: Q loads, pipeline fill and drain, the
+// epilogue, counted in tiles; no header when every request with work has
+// the same length, whose equal ranges then fall on request boundaries)
+// followed by its T_r real tiles, in request order.  The runs, TV tiles in
+// all, are cut into ranges of L = ceil(TV / N)
+// tiles, N = min(plan_target, ceil(TV / plan_min_chunk)); workgroup w takes
+// [w L, (w + 1) L).  It walks the requests whose real tiles its range
+// covers: a request inside one range is written directly to the caller's
+// output; a request cut by a range boundary leaves one partial per range it
+// touches, in slot w for the range's first segment and plan_target + w for
+// its last (so a uniform batch's partials are contiguous, by range).
+// Workgroup (0, 0, 0) writes each request's merge record (StreamRecord).
+// All plan arithmetic is 32-bit: the host uses this plan only while every
+// virtual tile count fits in 31 bits.
+struct StreamPlan {
+  int A, E;  // this workgroup's virtual tiles [A, E)
+  int r;     // request whose run holds tile A (-1: nothing to do)
+  int V;     // first virtual tile of request r's run
+  int h;     // header tiles of every run
+};
+
+struct StreamCut {
+  int N, L;  // ranges and their length in virtual tiles
+};
+__device__ __forceinline__ StreamCut stream_cut(int TV, const DecodeArgs& a) {
+  if (TV <= 0) return StreamCut{0, 1};
+  const int n = (TV + a.plan_min_chunk - 1) / a.plan_min_chunk;
+  const int N = n < a.plan_target ? n : a.plan_target;
+  const int L = (TV + N - 1) / N;
+  return StreamCut{(TV + L - 1) / L, L};
+}
+// Merge record of a request whose run is the virtual tiles [v0, v1).
+__device__ __forceinline__ int4 stream_record(int v0, int v1, int header, StreamCut c, int slots) {
+  if (v1 == v0) return make_int4(0, 0, 0, kStreamEmpty);
+  const int wa = (v0 + header) / c.L, wb = (v1 - 1) / c.L;  // ranges of its first and last real tile
+  if (wa == wb) return make_int4(wa, wb, 0, kStreamDirect);
+  // range wa starts inside the run (header included): the request is its first segment
+  return make_int4(wa, wb, wa * c.L >= v0 ? wa : slots + wa, kStreamParts);
 }
 
-// The same plan for batches of at most 64 requests, computed by every wave
-// on its own: request r's tile count sits in lane r, and every sum, prefix
-// and search is a wave reduction, so the plan needs no LDS and no barrier.
-// Gives the same items as plan_item.
-__device__ int4 plan_item_wave(const DecodeArgs& a) {
+// Tiles of request r's clipped range (scalar loads).
+__device__ __forceinline__ int request_tiles(const DecodeArgs& a, int r) {
+  const int lo = max(a.tok_lo, 0);
+  const int cap = a.max_pages << a.page_shift;
+  const int h = min(min(a.tok_hi, ((const int32_t __attribute__((address_space(4)))*)a.seq_lens)[r]), cap);
+  return h > lo ? (h + kTileTok - 1) / kTileTok - lo / kTileTok : 0;
+}
+
+// The plan for batches of at most 64 requests, by every wave on its own:
+// request r's run length in lane r, sums and prefixes as wave reductions
+// (no LDS, no barrier).
+__device__ StreamPlan stream_plan_wave(const DecodeArgs& a) {
   const int lane = threadIdx.x & 63;
   const int lo = max(a.tok_lo, 0);
-  const int first = lo / kTileTok;
   const int cap = a.max_pages << a.page_shift;
   int nt = 0;  // tiles of request `lane`
   if (lane < a.num_reqs) {
-    const int h = min(min(a.tok_hi, a.seq_lens[lane]), cap);
-    nt = h > lo ? (h + kTileTok - 1) / kTileTok - first : 0;
+    const int hi = min(min(a.tok_hi, a.seq_lens[lane]), cap);
+    nt = hi > lo ? (hi + kTileTok - 1) / kTileTok - lo / kTileTok : 0;
   }
-  auto wsum = [](int v) {
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-    return v;
-  };
-  long long total = nt;
-  for (int d = 32; d >= 1; d >>= 1) total += __shfl_xor(total, d, 64);
-  const long long full_cap = (long long)a.plan_target * a.plan_max_chunk;
-  int chunk = total >= full_cap ? a.plan_max_chunk
-                                : max(a.plan_min_chunk, ((int)total + a.plan_target - 1) / a.plan_target);
-  auto items_at = [&](int c) { return wsum(nt / c + ((nt % c) ? 1 : 0)); };
-  // a ragged batch whose items overflow one round takes the shortest chunk
-  // that fits, if any chunk up to the maximum does (as plan_item)
-  if (items_at(chunk) > a.plan_target && chunk < a.plan_max_chunk && items_at(a.plan_max_chunk) <= a.plan_target) {
-    int lo_c = chunk, hi_c = a.plan_max_chunk;  // items_at(lo_c) > target >= items_at(hi_c)
-    while (hi_c - lo_c > 1) {
-      const int mid = (lo_c + hi_c) >> 1;
-      if (items_at(mid) <= a.plan_target) hi_c = mid;
-      else lo_c = mid;
-    }
-    chunk = hi_c;
+  int tmax = nt, tmin = nt > 0 ? nt : INT_MAX;
+  for (int d = 32; d >= 1; d >>= 1) {
+    tmax = max(tmax, __shfl_xor(tmax, d, 64));
+    tmin = min(tmin, __shfl_xor(tmin, d, 64));
   }
-  // full chunks numbered in request order, then one remainder per request
-  const int nf = nt / chunk, nr = (nt % chunk) ? 1 : 0;
-  int fi = nf, ri = nr;  // inclusive prefix sums over the requests
+  const int header = tmin == tmax ? 0 : a.plan_header;
+  const int nv = nt > 0 ? nt + header : 0;  // virtual tiles of request `lane`
+  int incl = nv;
   for (int d = 1; d < 64; d <<= 1) {
-    const int uf = __shfl_up(fi, d, 64), ur = __shfl_up(ri, d, 64);
-    if (lane >= d) {
-      fi += uf;
-      ri += ur;
+    const int u = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += u;
+  }
+  const int excl = incl - nv;
+  const int TV = __shfl(incl, 63, 64);
+  const StreamCut c = stream_cut(TV, a);
+  if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x < 64 && lane < a.num_reqs)
+    a.req_info[lane] = stream_record(excl, incl, header, c, a.plan_target);
+  const int w = blockIdx.x;
+  if (w >= c.N) return StreamPlan{0, 0, -1, 0, 0};
+  const int A = w * c.L, E = min(A + c.L, TV);  // the last range ends with the batch
+  // the first run ending past A holds tile A (empty requests have no run)
+  const unsigned long long bal = __ballot(lane < a.num_reqs && incl > A);
+  const int r = __ffsll((long long)bal) - 1;
+  return StreamPlan{A, E, r, __builtin_amdgcn_readlane(excl, r), header};
+}
+
+// The same plan for batches of up to kPlanMaxReqs requests, by the
+// workgroup: thread t sums the runs of requests [t * per, t * per + per), a
+// wave scan and the waves' totals through LDS give every prefix.  `scratch`
+// (LDS, >= 3 NT / 64 + 2 ints) is free again on return.
+template <int NT>
+__device__ StreamPlan stream_plan_block(const DecodeArgs& a, int32_t* scratch) {
+  constexpr int NWV = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (a.num_reqs + NT - 1) / NT;
+  // equal lengths?  (max and min over the requests with work)
+  int tmax = 0, tmin = INT_MAX;
+  for (int k = 0; k < per; ++k) {
+    const int r = tid * per + k;
+    if (r < a.num_reqs) {
+      const int t = request_tiles(a, r);
+      tmax = max(tmax, t);
+      if (t > 0) tmin = min(tmin, t);
     }
   }
-  const int F = __shfl(fi, 63, 64);
-  const int foff = fi - nf;
-  const int rslot = nr ? F + ri - nr : -1;
-  const int me = blockIdx.x;
-  if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x < 64 && lane < a.num_reqs)
-    a.req_info[lane] = make_int4(foff, nf, rslot, 0);
-  const bool mine = lane < a.num_reqs && ((me >= foff && me < foff + nf) || me == rslot);
-  const unsigned long long bal = __ballot(mine);
-  if (bal == 0) return make_int4(-1, 0, 0, me);
-  const int r = __ffsll((long long)bal) - 1;  // the one request holding item me
-  const int r_foff = __builtin_amdgcn_readlane(foff, r);
-  const int r_nf = __builtin_amdgcn_readlane(nf, r);
-  const int r_nt = __builtin_amdgcn_readlane(nt, r);
-  const bool full = me < r_foff + r_nf;
-  const int t0 = full ? first + (me - r_foff) * chunk : first + r_nf * chunk;
-  const int t1 = full ? t0 + chunk : first + r_nt;
-  return make_int4(r, __builtin_amdgcn_readfirstlane(t0), __builtin_amdgcn_readfirstlane(t1), me);
+  for (int d = 32; d >= 1; d >>= 1) {
+    tmax = max(tmax, __shfl_xor(tmax, d, 64));
+    tmin = min(tmin, __shfl_xor(tmin, d, 64));
+  }
+  int* wsum = scratch;                // [NWV]
+  int* found = scratch + NWV;         // {r, V}
+  int* ext = scratch + NWV + 2;       // [NWV][2]: each wave's max and min
+  if (lane == 0) {
+    ext[2 * wave] = tmax;
+    ext[2 * wave + 1] = tmin;
+  }
+  __syncthreads();
+  for (int w = 0; w < NWV; ++w) {
+    tmax = max(tmax, ext[2 * w]);
+    tmin = min(tmin, ext[2 * w + 1]);
+  }
+  const int header = tmin == tmax ? 0 : a.plan_header;
+  auto run = [&](int r) {
+    const int t = request_tiles(a, r);
+    return t > 0 ? t + header : 0;
+  };
+  int mine = 0;
+  for (int k = 0; k < per; ++k) {
+    const int r = tid * per + k;
+    if (r < a.num_reqs) mine += run(r);
+  }
+  int incl = mine;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += u;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  if (tid == 0) found[0] = -1;
+  __syncthreads();
+  int before = 0, TV = 0;
+  for (int w = 0; w < NWV; ++w) {
+    if (w < wave) before += wsum[w];
+    TV += wsum[w];
+  }
+  const StreamCut c = stream_cut(TV, a);
+  const int w = blockIdx.x;
+  const bool active = w < c.N;
+  const int A = w * c.L, E = min(A + c.L, TV);  // the last range ends with the batch
+  const bool writer = blockIdx.x == 0 && blockIdx.z == 0;
+  int v = before + incl - mine;  // first virtual tile of this thread's first request
+  for (int k = 0; k < per; ++k) {
+    const int r = tid * per + k;
+    if (r >= a.num_reqs) break;
+    const int nv = run(r);
+    if (writer) a.req_info[r] = stream_record(v, v + nv, header, c, a.plan_target);
+    if (active && v <= A && A < v + nv) {  // exactly one run holds tile A
+      found[0] = r;
+      found[1] = v;
+    }
+    v += nv;
+  }
+  __syncthreads();
+  const StreamPlan p{A, E, active ? found[0] : -1, found[1], header};
+  __syncthreads();
+  return p;
 }
 
 template <int D_QK, int D_V, int WH, int WV>
@@ -401,33 +371,31 @@ template <int D_QK, int D_V, int WH, int WV, bool TBL>
 __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const DecodeArgs a) {
   using C = Cfg<D_QK, D_V, WH, WV>;
   static_assert(!TBL || (C::NW == 4 && !C::PADDED && !C::KSPLIT && C::DMA_W <= 9 &&
-                         C::BODY_B + 4 * kTblTiles * 8 <= C::SMEM_B),
+                         C::BODY_B + 4 * kTblTiles * 4 <= C::SMEM_B && D_QK * 2 % 128 == 0),
                 "tile-address table layout");
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_B];
   // this chunk's physical page ids; with the split score contraction only
   // the plan's scratch, in the (then unused) exchange area
   int32_t* const page_lds = (int32_t*)(smem + (C::KSPLIT ? C::RING_B : C::BODY_B));
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // One segment: tiles [t_begin, t_end) of request b, its result written to
+  // the caller's output (partial = false) or to partial row prow + head.
+  // The arguments come in through `a`, a reference the segment loop below
+  // hides from the optimiser, so that their loads are not hoisted out of the
+  // loop and held in scalar registers across every segment.
+  auto segment = [&](const DecodeArgs& a, const int b, const int t_begin, const int t_end, const int64_t prow,
+                     const bool partial) {
+  // Per-lane values are derived here from a thread index the optimiser
+  // cannot see as loop invariant (held across segments they would take
+  // registers from the tile loop).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wh = wave % WH;
   const int wv = wave / WH;
   const int g = lane >> 5;   // k-group of the 32x32x16 operands
   const int n = lane & 31;   // head column (B / C operands), token row (A operand of QK)
-
-  // Work item: request b and its tile range; `split` is the partial-output
-  // slot.  In work-list mode the item comes from the plan below, otherwise
-  // from the grid.
-  int b = blockIdx.y, split = blockIdx.x;
-  int4 item = make_int4(0, 0, 0, 0);
-  const bool worklist = a.plan_target > 0;
-  if (worklist) {
-    item = a.num_reqs <= 64 ? plan_item_wave(a) : plan_item<C::NTHREADS>(a, page_lds);
-    if (item.x < 0) return;  // beyond the plan's items
-    b = item.x;
-    split = item.w;
-  }
-  const int b_out = worklist ? 0 : b;  // request term of the output row index
   // this workgroup's KV head and its query heads [k_lo, k_hi) within the share
   const int zk = blockIdx.z / a.z_per_kv;
   const int zz = blockIdx.z - zk * a.z_per_kv;
@@ -439,39 +407,29 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   const int hs = head0 + n;                      // this lane's head within the share
   const bool head_ok = hs < k_hi;
   const int hs_safe = head_ok ? hs : 0;
-
+  const int lo = max(a.tok_lo, 0);
   // Read-only tables through the constant address space: scalar loads, so
   // the vector-memory counter only ever counts the KV DMA.
   const int32_t __attribute__((address_space(4)))* bt_row =
       (const int32_t __attribute__((address_space(4)))*)(a.bt + (int64_t)b * a.max_pages);
   const int seq = ((const int32_t __attribute__((address_space(4)))*)a.seq_lens)[b];
-
-  // ---- this workgroup's token range ----
   // tokens beyond the block table's capacity are never read
-  const int lo = max(a.tok_lo, 0);
   const int hi = min(min(a.tok_hi, seq), a.max_pages << a.page_shift);
-  int t_begin = 0, t_end = 0;  // absolute tile indices [t_begin, t_end)
-  if (worklist) {
-    t_begin = item.y;
-    t_end = item.z;
-  } else if (hi > lo) {
-    const int tf = lo / kTileTok;
-    const int nt = (hi + kTileTok - 1) / kTileTok - tf;
-    const int chunk = a.fixed_splits > 0 ? (nt + a.fixed_splits - 1) / a.fixed_splits : a.chunk_tiles;
-    t_begin = tf + split * chunk;
-    t_end = min(t_begin + chunk, tf + nt);
-  }
   const int mlo = max(lo, t_begin * kTileTok);
   const int mhi = min(hi, t_end * kTileTok);
 
-  float* out_row = a.out + split * a.out_split_stride + ((int64_t)b_out * a.n_heads + hs_safe) * D_V;
-  float* lse_ptr =
-      a.lse ? a.lse + split * a.lse_split_stride + (int64_t)b_out * a.n_heads + hs_safe : nullptr;
+  float* out_row = a.out + ((int64_t)b * a.n_heads + hs_safe) * D_V;
+  // the caller's LSE (a partial's LSE goes beside each of its group scales)
+  float* lse_ptr = (!partial && a.lse) ? a.lse + (int64_t)b * a.n_heads + hs_safe : nullptr;
+  constexpr int NG = D_V / partial_group_cols(D_V, WV);  // scale groups of a partial row
+  constexpr int GW = NG / WV;                            // ... of them in this wave's V columns
+  // partial row record of this lane's head: {LSE, 2^e} per column group
+  float2* const prec = (float2*)a.part_l + (prow + hs_safe) * NG + wv * GW;
 
   if (t_end <= t_begin) {  // empty chunk: O = 0, LSE = -inf
     // A split-KV partial with LSE = -inf is never read by the merge, so only
     // the LSE is written there; the caller's own output gets the zeros.
-    if (head_ok && !a.partial_out) {
+    if (head_ok && !partial) {
 #pragma unroll
       for (int vb = 0; vb < C::VB; ++vb)
 #pragma unroll
@@ -481,6 +439,10 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
         }
     }
     if (head_ok && lse_ptr && wv == 0 && g == 0) *lse_ptr = -INFINITY;
+    if (head_ok && partial && g == 0) {
+#pragma unroll
+      for (int k = 0; k < GW; ++k) prec[k] = float2{-INFINITY, 1.0f};
+    }
     return;
   }
   const int ntiles = t_end - t_begin;
@@ -619,20 +581,20 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     lds_dma16_s(base, (uint32_t)(row * row_b + chunk * 16), d.lds + nn * 1024);
   };
 
-  // Tile-address table (TBL): entry [w][i] is the pool address of the first
-  // row of wave w's row group in tile i of the chunk, i.e. of token
-  // clamp(32 (t_begin + i) + 8w, mlo, mhi - 1); the group's other rows are
-  // at most 7 rows further on the same page.  The lane offset is the same
-  // for every interior tile; the first and last tiles clamp rows outside
-  // [mlo, mhi) to the nearest valid row of the group.
-  uint64_t* const tbl = (uint64_t*)(smem + C::BODY_B) + (TBL ? wave * kTblTiles : 0);
+  // Tile-address table (TBL): entry [w][i] locates the first row of wave w's
+  // row group in tile i of the chunk, i.e. of token clamp(32 (t_begin + i) +
+  // 8w, mlo, mhi - 1), as its byte offset from this KV head's base in units
+  // of 128 B (rows, pages and the head offset are multiples of 128 B for
+  // 576-wide rows; 32 bits cover pools of up to 512 GiB).  The group's other
+  // rows are at most 7 rows further on the same page.  The lane offset is
+  // the same for every interior tile; the first and last tiles clamp rows
+  // outside [mlo, mhi) to the nearest valid row of the group.
+  uint32_t* const tbl = (uint32_t*)(smem + C::BODY_B) + (TBL ? wave * kTblTiles : 0);
   const uint32_t chunk_off = 16u * ((uint32_t)(lane & 7) ^ row_swizzle(8 * wave + l8));
   const uint32_t voff_int = (uint32_t)(l8 * row_b) + chunk_off;
-  auto tbl_plan = [&](uint64_t entry, int i, int slot) -> DmaPlan {
+  auto tbl_plan = [&](uint32_t entry, int i, int slot) -> DmaPlan {
     DmaPlan d{};
-    const uint32_t lo32 = __builtin_amdgcn_readfirstlane((uint32_t)entry);
-    const uint32_t hi32 = __builtin_amdgcn_readfirstlane((uint32_t)(entry >> 32));
-    d.wbase = (const char*)(uintptr_t)(((uint64_t)hi32 << 32) | lo32);
+    d.wbase = (const char*)kv + ((uint64_t)__builtin_amdgcn_readfirstlane(entry) << 7);
     d.lds = smem_base + slot * C::TILE_B + wave * 1024;
     d.voff = voff_int;
     if (i == 0 || i == ntiles - 1) {
@@ -1043,9 +1005,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
           bad = true;
           pg = 0;
         }
-        const uint64_t addr = (uint64_t)(uintptr_t)kv + (uint64_t)pg * (uint64_t)(a.page_stride * 2) +
-                              (uint64_t)((tokw & ps_mask) * row_b);
-        if (i < ntiles) tbl[i] = addr;
+        const uint64_t off = (uint64_t)pg * (uint64_t)(a.page_stride * 2) + (uint64_t)((tokw & ps_mask) * row_b);
+        if (i < ntiles) tbl[i] = (uint32_t)(off >> 7);
       }
     }
     if (__any(bad)) bad_page = true;
@@ -1109,7 +1070,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     floatx16 s = qk_and_exp(it, kDma, true, dp, vring, sprev, pcur);
     DmaPlan dp_next = dp;
     const int tn = t_begin + it + 3;
-    uint64_t entry = 0;  // table entry of tile it + 3 (TBL), read early, used at the plan step
+    uint32_t entry = 0;  // table entry of tile it + 3 (TBL), read early, used at the plan step
     pv_and_max(it, s, pcur, vring, kDma, dp, [&](int i) {
       if constexpr (TBL) {
         if (i == kTblLoadStep && tn < t_end) entry = tbl[it + 3];
@@ -1159,14 +1120,16 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float lr_tot = lr_run + __shfl_xor(lr_run, 32, 64);
   const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
-  float amax = 0.0f;  // largest |partial output| this lane stores (fp16 range check)
+  float pscale[GW];  // partial rows: 2^e of each of this wave's column groups
   __syncthreads();
   {
     float* stage = (float*)smem + wave * 32 * C::PITCH;
-    float* out_base = a.out + split * a.out_split_stride + ((int64_t)b_out * a.n_heads + head0) * D_V;
+    float* out_base = a.out + ((int64_t)b * a.n_heads + head0) * D_V;
     constexpr int ROWF = C::PB * 32;  // staged floats per row and pass
+    static_assert(ROWF == partial_group_cols(D_V, WV) && C::VB / C::PB == GW, "scale groups as the host lays them out");
 #pragma unroll
     for (int pass = 0; pass < C::VB / C::PB; ++pass) {
+      float pm = 0.0f;  // largest |value| this lane stages (partial rows)
 #pragma unroll
       for (int vbl = 0; vbl < C::PB; ++vbl)
 #pragma unroll
@@ -1174,10 +1137,11 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
           floatx4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = oacc[pass * C::PB + vbl][4 * rq + e] * inv;
+          if (partial) pm = fmaxf(fmaxf(pm, fmaxf(fabsf(v[0]), fabsf(v[1]))), fmaxf(fabsf(v[2]), fabsf(v[3])));
           *(floatx4*)(stage + n * C::PITCH + vbl * 32 + rq * 8 + 4 * g) = v;
         }
       const int col0 = (wv * C::VB + pass * C::PB) * 32;
-      if (!a.partial_out) {
+      if (!partial) {
 #pragma unroll
         for (int i = 0; i < 32 * ROWF / 256; ++i) {
           const int e = (i * 64 + lane) * 4;
@@ -1186,30 +1150,115 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
           if (head0 + row < k_hi) *(floatx4*)(out_base + (int64_t)row * D_V + col0 + col) = v;
         }
       } else {
-        // split-KV partial: fp16, 16 bytes per lane (8 columns).  A value
-        // beyond the fp16 range is clamped to it and flagged.
-        _Float16* hbase = (_Float16*)a.out + split * a.out_split_stride + ((int64_t)b_out * a.n_heads + head0) * D_V;
+        // Split-KV partial: the pass's ROWF columns of a row (one column
+        // group) are stored in fp16 as O / 2^e, e >= 0 the smallest exponent
+        // that brings the group's largest |O| below 2^15; 2^e goes to the
+        // row's record for the merge.  The partial so keeps fp16's precision
+        // relative to its largest value for any finite input.  The row's
+        // 1 / 2^e sits in the staging row's padding.
+        pm = fmaxf(pm, __shfl_xor(pm, 32, 64));  // the head's other half of the columns
+        // e = max(0, exponent of pm - 15), read off the float's bits (pm =
+        // m 2^(E - 126), m in [0.5, 1), E the biased exponent)
+        const int sh = max(0, (int)((__float_as_uint(pm) >> 23) & 0xffu) - 141);
+        pscale[pass] = __uint_as_float((uint32_t)(127 + sh) << 23);
+        _Float16* hbase = (_Float16*)a.part_o + (prow + head0) * D_V;
+        // rows of ordinary magnitude (every |O| < 2^15, e = 0: the common
+        // case) are converted as they are; the scaled form (rare) is kept
+        // as a loop, so that its code stays small
+        if (__any(sh > 0)) {
+          if (g == 0) stage[n * C::PITCH + ROWF] = __uint_as_float((uint32_t)(127 - sh) << 23);
+#pragma unroll 1
+          for (int i = 0; i < 32 * ROWF / 512; ++i) {
+            const int e = (i * 64 + lane) * 8;
+            const int row = e / ROWF, col = e % ROWF;
+            const float isc = stage[row * C::PITCH + ROWF];
+            const floatx4 v0 = *(const floatx4*)(stage + row * C::PITCH + col);
+            const floatx4 v1 = *(const floatx4*)(stage + row * C::PITCH + col + 4);
+            halfx8 h;
 #pragma unroll
-        for (int i = 0; i < 32 * ROWF / 512; ++i) {
-          const int e = (i * 64 + lane) * 8;
-          const int row = e / ROWF, col = e % ROWF;
-          const floatx4 v0 = *(const floatx4*)(stage + row * C::PITCH + col);
-          const floatx4 v1 = *(const floatx4*)(stage + row * C::PITCH + col + 4);
-          halfx8 h;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const float x = k < 4 ? v0[k] : v1[k - 4];
-            amax = fmaxf(amax, fabsf(x));
-            h[k] = (_Float16)__builtin_amdgcn_fmed3f(x, -kHalfMax, kHalfMax);
+            for (int k = 0; k < 8; ++k) h[k] = (_Float16)((k < 4 ? v0[k] : v1[k - 4]) * isc);
+            if (head0 + row < k_hi) *(halfx8*)(hbase + (int64_t)row * D_V + col0 + col) = h;
           }
-          if (head0 + row < k_hi) *(halfx8*)(hbase + (int64_t)row * D_V + col0 + col) = h;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 32 * ROWF / 512; ++i) {
+            const int e = (i * 64 + lane) * 8;
+            const int row = e / ROWF, col = e % ROWF;
+            const floatx4 v0 = *(const floatx4*)(stage + row * C::PITCH + col);
+            const floatx4 v1 = *(const floatx4*)(stage + row * C::PITCH + col + 4);
+            halfx8 h;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) h[k] = (_Float16)(k < 4 ? v0[k] : v1[k - 4]);
+            if (head0 + row < k_hi) *(halfx8*)(hbase + (int64_t)row * D_V + col0 + col) = h;
+          }
         }
       }
     }
   }
-  if (__any(amax > kHalfMax) && lane == 0) atomicOr(a.dev_err, kDevErrPartialRange);
-  if (head_ok && lse_ptr && wv == 0 && g == 0)
-    *lse_ptr = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  const float lse_val = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  if (head_ok && lse_ptr && wv == 0 && g == 0) *lse_ptr = lse_val;
+  if (head_ok && partial && g == 0) {
+#pragma unroll
+    for (int k = 0; k < GW; ++k) prec[k] = float2{lse_val, pscale[k]};
+  }
+  };  // segment
+
+  // ---- the workgroup's segments ----
+  // Grid mode: one chunk of request blockIdx.y.  Stream mode: the requests
+  // the workgroup's range of the batch's tiles covers, in order.
+  const bool stream = a.plan_target > 0;
+  StreamPlan sp{0, 0, 0, 0, 0};
+  if (stream) {
+    sp = a.num_reqs <= 64 ? stream_plan_wave(a) : stream_plan_block<C::NTHREADS>(a, page_lds);
+    sp = StreamPlan{__builtin_amdgcn_readfirstlane(sp.A), __builtin_amdgcn_readfirstlane(sp.E),
+                    __builtin_amdgcn_readfirstlane(sp.r), __builtin_amdgcn_readfirstlane(sp.V),
+                    __builtin_amdgcn_readfirstlane(sp.h)};
+    if (sp.r < 0) return;
+  }
+  const int lo = max(a.tok_lo, 0);
+  int r = stream ? sp.r : blockIdx.y;
+  int V = sp.V;  // stream mode: first virtual tile of request r's run
+  for (int k = 0;; ++k) {
+    int t_begin = 0, t_end = 0, b = r;
+    int64_t prow = 0;
+    bool partial = false;
+    if (stream) {
+      // next request with real tiles in [A, E) (empty requests have no run;
+      // a range may end inside a run's header)
+      int nt = 0;
+      while (V < sp.E && r < a.num_reqs && (nt = request_tiles(a, r)) == 0) ++r;
+      const int R0 = V + sp.h;  // first real tile of the run
+      if (V >= sp.E || r >= a.num_reqs || R0 >= sp.E) break;
+      const int s0 = max(sp.A, R0), s1 = min(sp.E, R0 + nt);
+      b = r;
+      t_begin = lo / kTileTok + (s0 - R0);
+      t_end = lo / kTileTok + (s1 - R0);
+      partial = s0 != R0 || s1 != R0 + nt;
+      prow = (int64_t)(k > 0 ? a.plan_target + blockIdx.x : blockIdx.x) * a.n_heads;  // first or last segment
+      V = R0 + nt;
+      ++r;
+    } else {
+      if (k > 0) break;
+      const int seq = ((const int32_t __attribute__((address_space(4)))*)a.seq_lens)[b];
+      const int hi = min(min(a.tok_hi, seq), a.max_pages << a.page_shift);
+      if (hi > lo) {
+        const int tf = lo / kTileTok;
+        const int nt = (hi + kTileTok - 1) / kTileTok - tf;
+        const int chunk = a.fixed_splits > 0 ? (nt + a.fixed_splits - 1) / a.fixed_splits : a.chunk_tiles;
+        t_begin = tf + blockIdx.x * chunk;
+        t_end = min(t_begin + chunk, tf + nt);
+      }
+      partial = a.grid_partial != 0;
+      prow = ((int64_t)blockIdx.x * a.num_reqs + b) * a.n_heads;
+    }
+    if (k > 0) __syncthreads();  // the previous segment's epilogue is done with LDS
+    // the arguments as they lie in the kernel-argument segment (the launch's
+    // only argument), read through a pointer the optimiser cannot follow
+    typedef const DecodeArgs __attribute__((address_space(4)))* ArgPtr;
+    ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ap));
+    segment(*(const DecodeArgs*)ap, b, t_begin, t_end, prow, partial);
+  }
 }
 
 template <int D_QK, int D_V, int WH, int WV, bool TBL = false>
@@ -1225,7 +1274,9 @@ hipError_t launch_decode(const DecodeVariant& v, dim3 grid, const DecodeArgs& a,
                          hipEvent_t e1) {
   if (v.d_qk == 576 && v.d_v == 512) {
     if (v.wh == 4 && v.wv == 1) {
-      if (v.max_chunk_tiles <= kTblTiles) return launch_variant<576, 512, 4, 1, true>(grid, a, stream, e0, e1);
+      // the table holds kTblTiles tiles and 32-bit offsets in 128-byte units
+      if (v.max_chunk_tiles <= kTblTiles && (int64_t)a.num_pages * a.page_stride * 2 <= ((int64_t)1 << 39))
+        return launch_variant<576, 512, 4, 1, true>(grid, a, stream, e0, e1);
       return launch_variant<576, 512, 4, 1>(grid, a, stream, e0, e1);
     }
     if (v.wh == 2 && v.wv == 2) return launch_variant<576, 512, 2, 2>(grid, a, stream, e0, e1);

@@ -20,29 +20,33 @@ constexpr int kLdsParts = 2048;  // parts whose weights are kept in LDS (more ar
 constexpr int kBatch = 8;        // partial rows a thread loads before combining them
 
 // Parts of a row: either n_parts uniform parts at p * rows + row (the
-// public merge and grid-mode split-KV), or the parts the decode kernel
-// listed for the row's request (work-list split-KV).  at(row) resolves the
-// row once; the result maps a part number to the partial row it lives in.
+// public merge and grid-mode split-KV), or the parts of the row's request
+// in the decode kernel's stream plan.  at(row) resolves the row once; the
+// result maps a part number to the partial row it lives in, and `skip`
+// marks a row the decode kernel wrote itself.
 struct UniformRow {
   int n;
   int64_t row, rows;
+  bool skip;
   __device__ int64_t index(int p) const { return (int64_t)p * rows + row; }
 };
 struct UniformParts {
   int32_t n_parts, rows;
-  __device__ UniformRow at(int64_t row) const { return {n_parts, row, rows}; }
+  __device__ UniformRow at(int64_t row) const { return {n_parts, row, rows, false}; }
 };
-struct ListedRow {
-  int n, first, nfull, rem, hs, h;
-  __device__ int64_t index(int p) const { return (int64_t)(p < nfull ? first + p : rem) * hs + h; }
+struct StreamRow {
+  int n, first_slot, first_range, hs, h;
+  bool skip;
+  __device__ int64_t index(int p) const { return (int64_t)(p == 0 ? first_slot : first_range + p) * hs + h; }
 };
-struct ListedParts {
-  const int4* req_info;  // {first full-chunk slot, full chunks, remainder slot or -1, 0}
+struct StreamParts {
+  const int4* req_info;  // the decode kernel's merge record of each request
   int32_t hs;
-  __device__ ListedRow at(int64_t row) const {
+  __device__ StreamRow at(int64_t row) const {
     const int r = (int)row;  // rows = B * hs < 2^31
     const int4 info = req_info[r / hs];
-    return {info.y + (info.z >= 0 ? 1 : 0), info.x, info.y, info.z, hs, r % hs};
+    const int n = info.w == kStreamParts ? info.y - info.x + 1 : 0;
+    return {n, info.z, info.x, hs, r % hs, info.w == kStreamDirect};
   }
 };
 
@@ -171,28 +175,52 @@ struct Row8<float> {
   __device__ float get(int k) const { return k < 4 ? a[k] : b[k - 4]; }
 };
 
-template <typename T, typename Parts>
-__global__ void __launch_bounds__(256) split_merge_kernel(const T* __restrict__ P, const float* __restrict__ L,
-                                                          Parts parts, int32_t rows, int32_t d_v,
-                                                          float* __restrict__ out, float* __restrict__ lse_out) {
+// A part's LSE and the factor its stored values carry, for the columns of
+// one lane: the caller's partials (one LSE per row, values as given), or
+// the split-KV partials (per row and column group of 2^shift columns a
+// record {LSE, power of two the group's values were divided by}).
+struct PlainRecs {
+  const float* L;
+  __device__ float2 at(int64_t pi, int) const { return float2{L[pi], 1.0f}; }
+};
+struct GroupRecs {
+  const float2* R;
+  int32_t shift;
+  __device__ float2 at(int64_t pi, int col) const {
+    return R[(pi << (9 - shift)) + (col >> shift)];  // d_v = 512 columns: 2^(9 - shift) groups
+  }
+};
+struct GroupRecsAny {  // any d_v (a multiple of 2^shift)
+  const float2* R;
+  int32_t shift, groups;
+  __device__ float2 at(int64_t pi, int col) const { return R[pi * groups + (col >> shift)]; }
+};
+template <typename T, typename Parts, typename Recs>
+__global__ void __launch_bounds__(256) split_merge_kernel(const T* __restrict__ P, Recs recs, Parts parts,
+                                                          int32_t rows, int32_t d_v, float* __restrict__ out,
+                                                          float* __restrict__ lse_out) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= rows) return;
   const auto rp = parts.at(row);
+  if (rp.skip) return;
   const int n = rp.n;
   const int c = lane * 8;
   const bool active = c < d_v;
+  const int cc = active ? c : 0;  // lanes past d_v read column 0's record
   float M = -INFINITY, S = 0.0f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < n; p0 += kSplitBatch) {
-    float l[kSplitBatch];
+    float l[kSplitBatch], psc[kSplitBatch];
     Row8<T> v[kSplitBatch];
 #pragma unroll
     for (int u = 0; u < kSplitBatch; ++u) {
       const bool live = p0 + u < n;
       const int64_t pi = live ? rp.index(p0 + u) : 0;
-      l[u] = live ? L[pi] : -INFINITY;
+      const float2 rec = live ? recs.at(pi, cc) : float2{-INFINITY, 1.0f};
+      l[u] = rec.x;
+      psc[u] = rec.y;
       if (live && active) v[u].load(P + pi * d_v + c);
       else v[u].zero();
     }
@@ -208,9 +236,10 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const T* __restrict__ 
     for (int u = 0; u < kSplitBatch; ++u) {
       if (l[u] != -INFINITY) {
         const float w = __expf(l[u] - mb);
+        const float wv = w * psc[u];
         S += w;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] += w * v[u].get(k);
+        for (int k = 0; k < 8; ++k) acc[k] += wv * v[u].get(k);
       }
     }
     M = mb;
@@ -232,24 +261,38 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const T* __restrict__ 
   if (lse_out && lane == 0) lse_out[row] = M + __logf(S);
 }
 
-}  // namespace
-
-hipError_t launch_split_merge(const uint16_t* partials, const float* lses, int32_t n_parts, int32_t rows,
-                              int32_t d_v, float* out, float* lse_out, hipStream_t stream, hipEvent_t e0,
-                              hipEvent_t e1) {
-  if (rows == 0) return hipSuccess;
-  hipExtLaunchKernelGGL((split_merge_kernel<_Float16, UniformParts>), dim3((rows + 3) / 4), dim3(256), 0, stream, e0,
-                        e1, 0, (const _Float16*)partials, lses, UniformParts{n_parts, rows}, rows, d_v, out, lse_out);
+// The fp16 split-KV merge with the record layout of the decode kernel.
+template <typename Parts>
+hipError_t launch_fp16_merge(const uint16_t* partials, const float* recs, int32_t shift, Parts parts, int32_t rows,
+                             int32_t d_v, float* out, float* lse_out, hipStream_t stream, hipEvent_t e0,
+                             hipEvent_t e1) {
+  if (d_v == 512)
+    hipExtLaunchKernelGGL((split_merge_kernel<_Float16, Parts, GroupRecs>), dim3((rows + 3) / 4), dim3(256), 0,
+                          stream, e0, e1, 0, (const _Float16*)partials, GroupRecs{(const float2*)recs, shift}, parts,
+                          rows, d_v, out, lse_out);
+  else
+    hipExtLaunchKernelGGL((split_merge_kernel<_Float16, Parts, GroupRecsAny>), dim3((rows + 3) / 4), dim3(256), 0,
+                          stream, e0, e1, 0, (const _Float16*)partials,
+                          GroupRecsAny{(const float2*)recs, shift, d_v >> shift}, parts, rows, d_v, out, lse_out);
   return hipGetLastError();
 }
 
-hipError_t launch_split_merge_segmented(const uint16_t* partials, const float* lses, const int4* req_info,
-                                        int32_t rows, int32_t hs, int32_t d_v, float* out, float* lse_out,
-                                        hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+}  // namespace
+
+hipError_t launch_split_merge(const uint16_t* partials, const float* recs, int32_t sc_shift, int32_t n_parts,
+                              int32_t rows, int32_t d_v, float* out, float* lse_out, hipStream_t stream,
+                              hipEvent_t e0, hipEvent_t e1) {
   if (rows == 0) return hipSuccess;
-  hipExtLaunchKernelGGL((split_merge_kernel<_Float16, ListedParts>), dim3((rows + 3) / 4), dim3(256), 0, stream, e0,
-                        e1, 0, (const _Float16*)partials, lses, ListedParts{req_info, hs}, rows, d_v, out, lse_out);
-  return hipGetLastError();
+  return launch_fp16_merge(partials, recs, sc_shift, UniformParts{n_parts, rows}, rows, d_v, out, lse_out, stream,
+                           e0, e1);
+}
+
+hipError_t launch_split_merge_stream(const uint16_t* partials, const float* recs, int32_t sc_shift,
+                                     const int4* req_info, int32_t rows, int32_t hs, int32_t d_v, float* out,
+                                     float* lse_out, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  if (rows == 0) return hipSuccess;
+  return launch_fp16_merge(partials, recs, sc_shift, StreamParts{req_info, hs}, rows, d_v, out, lse_out, stream, e0,
+                           e1);
 }
 
 hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_parts, int32_t rows,
@@ -258,21 +301,13 @@ hipError_t launch_lse_merge(const float* partials, const float* lses, int32_t n_
   if (rows == 0) return hipSuccess;
   if (d_v % 8 == 0 && d_v <= 512) {
     // one wave per row, every load of a row in one round
-    hipExtLaunchKernelGGL((split_merge_kernel<float, UniformParts>), dim3((rows + 3) / 4), dim3(256), 0, stream, e0,
-                          e1, 0, partials, lses, UniformParts{n_parts, rows}, rows, d_v, out, lse_out);
+    hipExtLaunchKernelGGL((split_merge_kernel<float, UniformParts, PlainRecs>), dim3((rows + 3) / 4), dim3(256), 0,
+                          stream, e0, e1, 0, partials, PlainRecs{lses}, UniformParts{n_parts, rows}, rows, d_v, out,
+                          lse_out);
     return hipGetLastError();
   }
   hipExtLaunchKernelGGL(lse_merge_kernel<UniformParts>, dim3(rows), dim3(kMergeThreads), 0, stream, e0, e1, 0,
                         partials, lses, UniformParts{n_parts, rows}, d_v, out, lse_out);
-  return hipGetLastError();
-}
-
-hipError_t launch_lse_merge_segmented(const float* partials, const float* lses, const int4* req_info, int32_t rows,
-                                      int32_t hs, int32_t d_v, float* out, float* lse_out, hipStream_t stream,
-                                      hipEvent_t e0, hipEvent_t e1) {
-  if (rows == 0) return hipSuccess;
-  hipExtLaunchKernelGGL(lse_merge_kernel<ListedParts>, dim3(rows), dim3(kMergeThreads), 0, stream, e0, e1, 0,
-                        partials, lses, ListedParts{req_info, hs}, d_v, out, lse_out);
   return hipGetLastError();
 }
 

@@ -93,15 +93,18 @@ def test_repack_rejects_bad_arguments(splash):
 def test_plan_shapes(splash):
     # request-owned, 128 heads, 4,096 tokens: one head group, split to fill 256 CUs
     s, g, w = sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096)
-    # unforced splits are cut on the device from the real lengths: room for
-    # 256 full chunks plus one remainder per request, each a 128 x 512 fp16
-    # partial output and 128 fp32 LSEs, plus each request's 16-byte part list
+    # unforced splits are cut on the device from the real lengths into at
+    # most 256 equal ranges of the batch's tiles, each leaving at most two
+    # partials: 512 partial rows per head, each 512 fp16 values and an
+    # 8-byte {LSE, scale} record per 256-column group, plus each request's
+    # 16-byte merge record
     assert g == 1 and s == 16
-    per_item = 128 * 512 * 2 + 128 * 4
-    assert 272 * per_item + 16 * 16 <= w <= 272 * per_item + 4096
-    # forced splits: fp16 outputs, then fp32 LSEs (each part 256-byte aligned)
+    per_part = 128 * (512 * 2 + 2 * 8)
+    assert 512 * per_part + 16 * 16 <= w <= 512 * per_part + 1024
+    # forced splits: fp16 outputs, then the records (each 256-byte aligned);
+    # a 16-head slice stores 128-column groups
     s, g, w = sp.decode_plan(16, 128, 576, 512, 64, 256, 4096, 0.07, 0, 16, 0, 16384, num_splits=8)
-    assert s == 8 and g == 1 and w == 8 * 16 * 16 * 512 * 2 + 8 * 16 * 16 * 4
+    assert s == 8 and g == 1 and w == 8 * 16 * 16 * 512 * 2 + 4 * 8 * 16 * 16 * 8
     # a 64-head slice uses 32-head x 2 waves groups
     s, g, _ = sp.decode_plan(2, 128, 576, 512, 64, 8, 16, 0.07, 0, 64, 0, 512)
     assert g == 1
@@ -199,4 +202,4 @@ def test_noalloc_rejects_a_share_beyond_its_scratch(splash):
     p = 0x1000
     rc = L.splash_decode_attn_noalloc(ctypes.byref(d), p, p, p, p, 0, 128, 0, 4096, p, None, None)
     assert rc == sp.EINVAL and b"scratch" in L.splash_last_error()
-    assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_splits=64)[2] > 64 << 20
+    assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_splits=64)[2] > 72 << 20

@@ -234,26 +234,33 @@ def test_transition_decode(transition):
                      quiet=True)
 
 
-def _items_at(tiles, c):
-    return int(sum((t + c - 1) // c for t in tiles))
+def _ranges(tiles, target=256, min_chunk=4):
+    """The device plan's cut of a batch's tiles: N equal contiguous ranges."""
+    T = sum(tiles)
+    N = min(target, -(-T // min_chunk))
+    return T, N, [w * T // N for w in range(N + 1)]
 
 
-def test_ragged_batch_searched_chunk_length():
-    """A ragged batch of 64 requests whose remainder chunks overflow one round
-    of workgroups at the first chunk length, so the device plan searches for
-    a longer one; 8 heads of d_qk 80 keep the oracle cheap.  Every request is
-    compared."""
+def test_ragged_batch_packed_ranges():
+    """A ragged batch of 64 requests cut into equal ranges of the batch's
+    tiles: ranges that hold several whole requests (written directly), and
+    requests spread over several ranges (merged); 8 heads of d_qk 80 keep the
+    oracle cheap.  Every request is compared."""
     lens = W.loguniform_lengths(71, 64, 40, 9000)
     tiles = [(int(n) + 31) // 32 for n in lens]
-    first = max(4, min(128, -(-sum(tiles) // 256)))
-    # the plan's first length overflows 256 items, the longest allowed one fits
-    assert _items_at(tiles, first) > 256 >= _items_at(tiles, 128)
+    T, N, cut = _ranges(tiles)
+    starts = np.concatenate([[0], np.cumsum(tiles)])
+    per_range = [int(np.sum((starts[:-1] >= cut[w]) & (starts[1:] <= cut[w + 1]))) for w in range(N)]
+    spans = [int(np.searchsorted(cut, starts[r + 1], side="left") - np.searchsorted(cut, starts[r], side="right") + 1)
+             for r in range(len(tiles))]
+    assert max(per_range) >= 2 and max(spans) >= 3
     c = W.make_decode_case("ragged80", 72, lens, num_heads=8, d_qk=80, d_v=64, page_size=16,
                            scale=1.0 / math.sqrt(80.0), std=0.5, extra_pages=4)
-    _print(f"case ragged d_qk 80: 64 requests, {sum(tiles)} tiles, first chunk {first}")
+    _print(f"case ragged d_qk 80: 64 requests, {T} tiles in {N} ranges; up to {max(per_range)} whole requests "
+           f"in a range, up to {max(spans)} ranges per request")
     go, gl = run_decode(c)
     ro, rl = run_oracle(c)
-    assert_close(go, gl, ro, rl, what="ragged d_qk 80, searched chunk")
+    assert_close(go, gl, ro, rl, what="ragged d_qk 80, packed ranges")
     for b in range(c.num_reqs):
         assert_close(go[b:b + 1], gl[b:b + 1], ro[b:b + 1], rl[b:b + 1], what=f"ragged80 request {b}", quiet=True)
 
@@ -445,27 +452,23 @@ def test_bad_page_index_is_flagged_not_faulted():
     assert sp.device_errors(clear=True) & sp.DEVERR_BAD_PAGE
 
 
-def test_partial_range_is_clamped_and_flagged():
-    """Split-KV partial outputs are kept in fp16.  V values near 1e5 (q scaled
-    down by the same factor, so the scores keep their N(0,1)-input scale): a
-    call without splits keeps fp32 throughout and matches the oracle; with
-    splits the partials exceed the fp16 range, are clamped (finite) and raise
-    the device error bit."""
+@pytest.mark.parametrize("f", [1e5, 1e30])
+def test_split_partials_keep_the_range(f):
+    """Split-KV partial outputs are kept in fp16 with a power-of-two scale per
+    row, so a split share keeps the range of any finite input.  V values near
+    f (q scaled down by f, so the scores keep their N(0,1)-input scale): with
+    and without splits the result matches the oracle (compared at 1/f) and no
+    device error bit is raised."""
     c = W.make_decode_case("big_v", 45, [700, 300], num_heads=128, d_qk=576, d_v=512, page_size=64,
                            scale=W.LATENT_SCALE)
-    f = 1e5
     kv = c.kv_pages.copy()
-    kv[..., :c.d_v] = W.bf16_bits((kv[..., :c.d_v].astype(np.uint32) << 16).view(np.float32) * f)
-    q = W.bf16_bits((c.q.astype(np.uint32) << 16).view(np.float32) / f)
+    kv[..., :c.d_v] = W.bf16_bits((kv[..., :c.d_v].astype(np.uint32) << 16).view(np.float32) * np.float32(f))
+    q = W.bf16_bits((c.q.astype(np.uint32) << 16).view(np.float32) / np.float32(f))
     c2 = W.DecodeCase(**{**c.__dict__, "kv_pages": kv, "q": q})
-    sp.device_errors(clear=True)
-    go, gl = run_decode(c2, num_splits=1)
-    assert not sp.device_errors(clear=True) & sp.DEVERR_PARTIAL_RANGE
     ro, rl = run_oracle(c2)
-    assert_close(go / f, gl, ro / f, rl, what="V near 1e5, no split")
-    gs, _ = run_decode(c2, num_splits=4)
-    assert sp.device_errors(clear=True) & sp.DEVERR_PARTIAL_RANGE
-    assert np.all(np.isfinite(gs)) and np.abs(gs).max() <= 65504.0
+    for splits in (1, 4, 0):
+        go, gl = run_decode(c2, num_splits=splits)
+        assert_close(go / f, gl, ro / f, rl, what=f"V near {f:.0e}, splits={splits}")
 
 
 @pytest.mark.parametrize("d_v", [512, 516])  # one wave per row; the workgroup form (d_v not a multiple of 8)
