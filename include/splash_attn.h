@@ -58,9 +58,9 @@ extern "C" {
 /* Device error bits (splash_device_errors). */
 #define SPLASH_DEVERR_BAD_PAGE 1      /* decode: block-table entry outside [0, num_pages) */
 #define SPLASH_DEVERR_REPACK_PAIR 2   /* repack: a pair was rejected (see splash_kv_repack) */
-#define SPLASH_DEVERR_PARTIAL_RANGE 4 /* decode: a split-KV partial output value exceeded the fp16
-                                         range (|x| > 65504) and was clamped; the merged output of
-                                         that request is inexact */
+#define SPLASH_DEVERR_PARTIAL_RANGE 4 /* reserved; no longer raised (split-KV partials carry a
+                                         power-of-two scale per row and column group, so no value is
+                                         clamped) */
 
 /* Shape of a paged latent-KV decode batch. */
 typedef struct splash_desc {
@@ -100,12 +100,14 @@ typedef struct splash_desc {
  *   out          fp32 [num_reqs][head_hi - head_lo][d_v]
  *   lse          fp32 [num_reqs][head_hi - head_lo], or NULL
  * The work is split into KV chunks (split-KV) when the share is too small to
- * fill the GPU; partials then go to a library-owned workspace and are merged
- * on the same stream.  A partial output is kept in fp16 (its LSE in fp32)
- * between the two kernels; a value beyond the fp16 range is clamped and
- * raises SPLASH_DEVERR_PARTIAL_RANGE.  Every KV head the share touches is
- * served by the same launch (one decode kernel, plus one merge kernel when
- * split).
+ * fill the GPU: the kernel cuts the batch's tiles (32 tokens each) into
+ * equal ranges from the device's seq_lens, a request inside one range is
+ * written directly, and a request cut by range boundaries leaves partials in
+ * a library-owned workspace that a merge kernel on the same stream combines.
+ * A partial output is kept in fp16 divided by a power of two per row and
+ * 128- or 256-column group (so any finite value keeps fp16's relative
+ * precision), its LSE in fp32.  Every KV head the share touches is served by
+ * the same launch (one decode kernel, plus one merge kernel when split).
  * Workspace: one per (device, stream), allocated on first need and grown on
  * demand (growth synchronises that stream, then frees the old buffer), freed
  * by splash_release_workspace.  Calls on different streams therefore never

@@ -11,7 +11,7 @@ namespace splash {
 // Device error bits (the SPLASH_DEVERR_* values of the public header).
 constexpr int32_t kDevErrBadPage = 1;
 constexpr int32_t kDevErrRepackPair = 2;
-constexpr int32_t kDevErrPartialRange = 4;
+constexpr int32_t kDevErrPartialRange = 4;  // reserved: no longer raised
 
 // Arguments of one decode-attention launch (passed by value to the kernel).
 struct DecodeArgs {

@@ -60,7 +60,6 @@ constexpr int kPageLds = 4096;  // page ids of a chunk staged in LDS (16 KiB)
 constexpr int kVPages = 4;      // VGPRs of page ids per lane: chunks of up to 256 pages
 constexpr int kLdsBytes = 160 * 1024 - kPageLds * 4;
 constexpr int kMaxBuf = 4;
-constexpr float kHalfMax = 65504.0f;  // largest finite fp16 (split-KV partials are stored in fp16)
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p = exp2(s - m) stays <= 256
 constexpr int kPlanStep = 22;  // PV MFMA after which the next tile's DMA plan is made (past the max slices)
 constexpr int kTblLoadStep = 12;  // PV MFMA after which the table entry of that plan is read
