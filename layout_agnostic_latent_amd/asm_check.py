@@ -42,11 +42,34 @@ def _regs(text: str) -> set:
 
 
 def scan(asm_text: str) -> list:
-    """Return (line number, message) for every access to an in-flight chain accumulator."""
+    """Return (line number, message) for every access to an in-flight chain accumulator.
+
+    Each chain's accumulator (the VGPR result of an inline-asm MFMA) is in
+    flight until _MIN_WAITS wait states have issued after its last MFMA:
+    every instruction counts as one, an s_nop N as N + 1.  Only the next MFMA
+    of the same chain may touch it earlier.  A label or a branch inside that
+    window is reported too: the wait states counted along the straight-line
+    code would not hold on another path.
+    """
     bad = []
     in_asm = False
-    pending = None  # (line index, registers) of the last inline-asm MFMA with a VGPR result
-    waits = 0
+    pending = {}  # accumulator registers -> [line index of its last MFMA, wait states since]
+
+    def flush(i, why):
+        for regs, (line, _) in list(pending.items()):
+            bad.append((i + 1, f"{why} inside the wait window of the accumulator written at line {line + 1}"))
+        pending.clear()
+
+    def tick(i, t, op, regs, n):
+        for key, st in list(pending.items()):
+            if regs & key:
+                bad.append((i + 1, f"accesses the in-flight accumulator of line {st[0] + 1}: {t}"))
+                del pending[key]
+                continue
+            st[1] += n
+            if st[1] >= _MIN_WAITS:
+                del pending[key]
+
     for i, line in enumerate(asm_text.split("\n")):
         t = line.strip()
         if t.startswith(";;#ASMSTART"):
@@ -55,34 +78,28 @@ def scan(asm_text: str) -> list:
         if t.startswith(";;#ASMEND"):
             in_asm = False
             continue
+        if re.match(r"^[.\w]+:", t):  # a label: another path may enter here
+            if pending:
+                flush(i, "label")
+            continue
         if not t or t.startswith(";") or t.startswith("."):
             continue
-        if t.endswith(":"):  # a label: another path may enter here
-            pending = None
-            continue
         op = t.split()[0]
+        if op.startswith("s_cbranch") or op.startswith("s_branch") or op.startswith("s_setpc"):
+            if pending:
+                flush(i, "branch")
+            continue
+        regs = _regs(t)
         if op.startswith("v_mfma"):
             m = _MFMA.match(t)
-            dst = _regs(m.group(1)) if m else set()
-            if pending is not None:
-                if dst == pending[1]:
-                    pending = None  # the chain continues: back-to-back accumulation is safe
-                elif _regs(t) & pending[1]:
-                    bad.append((i + 1, f"MFMA touches the in-flight accumulator of line {pending[0] + 1}: {t}"))
-                    pending = None
+            dst = frozenset(_regs(m.group(1))) if m else frozenset()
+            if dst in pending:
+                del pending[dst]  # the chain continues: back-to-back accumulation is safe
+            tick(i, t, op, regs, 1)
             if in_asm and m and m.group(1).startswith("v"):
-                pending, waits = (i, dst), 0
+                pending[dst] = [i, 0]
             continue
-        if pending is None:
-            continue
-        if op == "s_nop":
-            waits += int(t.split()[1]) + 1
-            if waits >= _MIN_WAITS:
-                pending = None
-            continue
-        if _regs(t) & pending[1]:
-            bad.append((i + 1, f"accesses the in-flight accumulator of line {pending[0] + 1}: {t}"))
-            pending = None
+        tick(i, t, op, regs, int(t.split()[1]) + 1 if op == "s_nop" else 1)
     return bad
 
 
@@ -100,7 +117,7 @@ def compile_asm(src: str = "decode_attn.hip") -> str:
 
 def main() -> int:
     text = compile_asm()
-    n_chain = sum(1 for l in text.split("\n") if "v_mfma" in l and "v[2:17]" in l)
+    n_chain = sum(1 for l in text.split("\n") if "v_mfma" in l and ("v[2:17]" in l or "v[18:33]" in l))
     bad = scan(text)
     for ln, msg in bad:
         print(f"decode_attn.s:{ln}: {msg}")

@@ -130,23 +130,45 @@ __device__ __forceinline__ float max_across_halves(float x) {
 // gives every MFMA of a kernel that uses AGPRs the AGPR form, and the score
 // tile would then have to share the AGPR file with the output accumulators
 // (which fill it).  Accumulating back to back into the same registers needs
-// no wait states; the last MFMA of a chain is followed by 20 wait states so
-// that VALU instructions may read its result.  The compiler takes an asm
-// statement's output as written when the statement issues, while the matrix
-// core writes it 8 passes later: a copy of the accumulator between two MFMAs
-// of a chain (a live-range split of the register allocator) would read it
-// in flight.  The accumulator is therefore pinned to fixed registers in
-// every statement of the chain, which leaves nothing to split.
+// no wait states.  The compiler takes an asm statement's output as written
+// when the statement issues, while the matrix core writes it 8 passes later:
+// a copy of the accumulator between two MFMAs of a chain (a live-range split
+// of the register allocator) would read it in flight.  The accumulator is
+// therefore pinned to fixed registers in every statement of the chain,
+// v[2:17] (R = 0) or v[18:33] (R = 1), which leaves nothing to split.
+// After the chain's last MFMA the VALU may read the result only 20 wait
+// states later: with W the last statement carries them as s_nops; without,
+// the caller issues at least 20 independent instructions first.
+template <int R>
 __device__ __forceinline__ void mfma_vgpr_first(floatx16& c, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "={v[2:17]}"(c) : "v"(a), "v"(b));
+  if constexpr (R == 0) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "={v[2:17]}"(c) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "={v[18:33]}"(c) : "v"(a), "v"(b));
 }
+template <int R>
 __device__ __forceinline__ void mfma_vgpr(floatx16& c, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+{v[2:17]}"(c) : "v"(a), "v"(b));
+  if constexpr (R == 0) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+{v[2:17]}"(c) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+{v[18:33]}"(c) : "v"(a), "v"(b));
 }
+// The chain's result held in its registers up to this point (so that no
+// copy of it is made while the matrix core may still be writing it).
+template <int R>
+__device__ __forceinline__ void chain_hold(floatx16& c) {
+  if constexpr (R == 0) asm volatile("" : "+{v[2:17]}"(c));
+  else asm volatile("" : "+{v[18:33]}"(c));
+}
+template <int R, bool W>
 __device__ __forceinline__ void mfma_vgpr_last(floatx16& c, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3"
-               : "+{v[2:17]}"(c)
-               : "v"(a), "v"(b));
+  if constexpr (!W) {
+    mfma_vgpr<R>(c, a, b);
+  } else if constexpr (R == 0) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+{v[2:17]}"(c)
+                 : "v"(a), "v"(b));
+  } else {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+{v[18:33]}"(c)
+                 : "v"(a), "v"(b));
+  }
 }
 
 // Balanced split-KV plan, computed by every workgroup from the device's
@@ -666,7 +688,12 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     if constexpr (C::KSPLIT) return kofs_w[s % KPAIRS] + C::SLAB_B * (s / KPAIRS);
     else return kofs[s & 3] + C::SLAB_B * (s >> 2);
   };
-  auto qk_tile = [&](int it, auto with_dma, bool do_dma, const DmaPlan& dp, auto&& hook) -> floatx16 {
+  // `reg` selects the chain's accumulator registers; without `waits` the
+  // caller must issue 20 independent instructions before reading the scores.
+  auto qk_tile = [&](int it, auto with_dma, bool do_dma, const DmaPlan& dp, auto&& hook, auto reg,
+                     auto waits) -> floatx16 {
+    constexpr int R = decltype(reg)::value;
+    constexpr bool W = decltype(waits)::value || C::KSPLIT;  // the score exchange reads them at once
     const char* tile = smem + (it % C::NBUF) * C::TILE_B;
     constexpr int PF = C::KPF < C::KSW ? C::KPF : C::KSW;
     floatx16 sacc;
@@ -676,9 +703,9 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
 #pragma unroll
     for (int s = 0; s < C::KSW; ++s) {
       const bf16x8 kf = kring[s % PF];
-      if (s == 0) mfma_vgpr_first(sacc, kf, qf[0]);
-      else if (s == C::KSW - 1) mfma_vgpr_last(sacc, kf, qf[s]);
-      else mfma_vgpr(sacc, kf, qf[s]);
+      if (s == 0) mfma_vgpr_first<R>(sacc, kf, qf[0]);
+      else if (s == C::KSW - 1) mfma_vgpr_last<R, W>(sacc, kf, qf[s]);
+      else mfma_vgpr<R>(sacc, kf, qf[s]);
       if (s + PF < C::KSW) kring[s % PF] = *(const bf16x8*)(tile + kaddr(s + PF));
       if constexpr (decltype(with_dma)::value) {
 #pragma unroll
@@ -834,7 +861,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // score MFMAs.  Returns tile j's scores and tile j-1's packed weights; the
   // sums of tile j-1's weights are added to the running sums.
   auto qk_and_exp = [&](int it, auto with_dma, bool do_dma, const DmaPlan& dp, bf16x8 (&vring)[PV_PF],
-                        floatx16& sprev, bf16x8 (&pcur)[2]) -> floatx16 {
+                        floatx16& sprev, bf16x8 (&pcur)[2], auto reg, auto waits) -> floatx16 {
     uint32_t pw[2][4];
     float lsum = 0.0f, lrsum = 0.0f;
     const float m = m_run;
@@ -843,7 +870,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
       vpf(sidx);
       const int t = sidx - kExpStep0;
       if (t >= 0 && t < kExpSlices) exp_slice(t, sprev, m, pw, lsum, lrsum);
-    });
+    }, reg, waits);
 #pragma unroll
     for (int t = C::KSW - kExpStep0; t < kExpSlices; ++t) exp_slice(t, sprev, m, pw, lsum, lrsum);
     l_run += lsum;
@@ -859,8 +886,13 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   //   7-9:        scaled max and the new running max.
   // After the products, the output and the running sums are rescaled to the
   // new max if it moved (lazily: only when it grew by more than 2^8).
+  // With the main loop's chains (no wait states of their own) the first
+  // slice reading the scores comes after kSlice0 PV steps of at least four
+  // instructions each.
+  constexpr bool kAltChains = TBL && !C::KSPLIT && C::NM >= 16;  // alternating chains, no chain wait states
+  constexpr int kSlice0 = kAltChains ? 6 : 0;
   auto pv_and_max = [&](int it, floatx16& s, const bf16x8 (&pcur)[2], bf16x8 (&vring)[PV_PF], auto with_dma,
-                        const DmaPlan& dp, auto&& extra) {
+                        const DmaPlan& dp, auto&& extra, auto reg) {
     // tiles of the main loop (with_dma) lie strictly inside the chunk: only
     // the first and the last tile can hold rows outside [mlo, mhi)
     if constexpr (!decltype(with_dma)::value) mask_tile(s, it);
@@ -881,41 +913,47 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
         for (int k = 0; k < ND; ++k)
           if ((k * C::NM) / ND == i) issue_one(dp, C::DMA_QK + k);
       }
-      if (i == 0) {
+      const int j = decltype(with_dma)::value ? i - kSlice0 : i;  // slice of this step
+      if constexpr (kAltChains && decltype(with_dma)::value) {
+        // the scores stay in the chain's registers until the wait states
+        // are covered (the PV steps before this one)
+        if (j == 0) chain_hold<decltype(reg)::value>(s);
+      }
+      if (j == 0) {
         mx[0] = max3(s[0], s[1], s[2]);
         mx[1] = max3(s[3], s[4], s[5]);
-      } else if (i == 1) {
+      } else if (j == 1) {
         mx[2] = max3(s[6], s[7], s[8]);
         mx[3] = max3(s[9], s[10], s[11]);
-      } else if (i == 2) {
+      } else if (j == 2) {
         mx[0] = max3(mx[0], mx[1], s[15]);
         mx[1] = max3(s[12], s[13], s[14]);
-      } else if (i == 3) {
+      } else if (j == 3) {
         mx[0] = max3(mx[0], mx[2], mx[3]);
-      } else if (i == 4) {
+      } else if (j == 4) {
         mx[0] = max3(mx[0], mx[1], mx[1]);
-      } else if (i == 5) {
+      } else if (j == 5) {
         // both halves of the head's column: lane l and lane l ^ 32
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[0]), __float_as_uint(mx[0]), false, false);
         mx[1] = __uint_as_float(r[0]);
         mx[2] = __uint_as_float(r[1]);
         pin(mx[1]);
         pin(mx[2]);
-      } else if (i == 6) {
+      } else if (j == 6) {
         mx[0] = max3(mx[1], mx[2], mx[2]);
-      } else if (i == 7) {
+      } else if (j == 7) {
         mx[0] *= a.scale_log2;
         pin(mx[0]);
-      } else if (i == 8) {
+      } else if (j == 8) {
         need = mx[0] > thr;
-      } else if (i == 9) {
+      } else if (j == 9) {
         m_new = need ? mx[0] : m_run;
         pin(m_new);
       }
     };
     pv_tile(it - 1, pcur, vring, step);
     // slices beyond the MFMA count (variants with fewer V blocks)
-    constexpr int kSteps = 10 > kPlanStep + 1 ? 10 : kPlanStep + 1;
+    constexpr int kSteps = 10 + kSlice0 > kPlanStep + 1 ? 10 + kSlice0 : kPlanStep + 1;
 #pragma unroll
     for (int i = C::NM; i < kSteps; ++i) step(i);
     const bool any_need = __any(need);
@@ -940,6 +978,10 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
 
   const std::integral_constant<bool, true> kDma;
   const std::integral_constant<bool, false> kNoDma;
+  const std::integral_constant<int, 0> kR0;
+  const std::integral_constant<int, 1> kR1;
+  const std::integral_constant<bool, true> kWaits;
+  const std::integral_constant<bool, false> kNoWaits;
 
   // Prologue.  Order of issue: the chunk's page ids, Q, then the first two
   // tiles' DMA.  The Q loads touch 32 rows per instruction and so keep the
@@ -1042,7 +1084,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     // own loads: with tile 1's DMA younger than Q, the last of those waits
     // also drain tile 1.  Tile 2's DMA is therefore issued after the scores,
     // not between them (it would be drained too).
-    floatx16 s = qk_tile(0, kNoDma, false, dp, [](int) {});
+    floatx16 s = qk_tile(0, kNoDma, false, dp, [](int) {}, kR0, kWaits);
     if (2 < ntiles) {
 #pragma unroll
       for (int k = 0; k < C::DMA_W; ++k) issue_one(dp, k);
@@ -1060,13 +1102,19 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // max, the page lookups and DMA plan of tile j+3 (scalar work, off the path
   // into the next scores).
   // One younger tile (j+1) stays in flight across the wait.
+  // With kAltChains consecutive iterations alternate the score chain's
+  // registers (tile j's scores stay in place while tile j+1's accumulate)
+  // and leave the chain's wait states to the PV steps before the first
+  // slice.
   int it = 1;
-  for (; it + 2 < ntiles; ++it) {
+  // One pipelined tile: the exponentials of `prev` under the tile's score
+  // chain, then its PV steps; returns the tile's scores.
+  auto iteration = [&](floatx16& prev, auto reg, auto waits) -> floatx16 {
     wait_vmcnt<C::DMA_W>();
     __syncthreads();
     bf16x8 vring[PV_PF];
     bf16x8 pcur[2];
-    floatx16 s = qk_and_exp(it, kDma, true, dp, vring, sprev, pcur);
+    floatx16 s = qk_and_exp(it, kDma, true, dp, vring, prev, pcur, reg, waits);
     DmaPlan dp_next = dp;
     const int tn = t_begin + it + 3;
     uint32_t entry = 0;  // table entry of tile it + 3 (TBL), read early, used at the plan step
@@ -1077,9 +1125,24 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
       } else {
         if (i == kPlanStep && tn < t_end) dp_next = dma_plan(tn, (it + 3) % C::NBUF, pages_of(tn));
       }
-    });
-    sprev = s;
+    }, reg);
     dp = dp_next;
+    return s;
+  };
+  if constexpr (kAltChains) {
+    // two scores variables, one per chain register block, so that neither
+    // chain's result is copied to carry it into the next tile
+    while (it + 2 < ntiles) {
+      floatx16 s1 = iteration(sprev, kR1, kNoWaits);
+      if (!(++it + 2 < ntiles)) {
+        sprev = s1;
+        break;
+      }
+      sprev = iteration(s1, kR0, kNoWaits);
+      ++it;
+    }
+  } else {
+    for (; it + 2 < ntiles; ++it) sprev = iteration(sprev, kR0, kWaits);
   }
   const DmaPlan none{nullptr, nullptr, 0u, 0, 0, nullptr, 0u};
   for (; it < ntiles; ++it) {
@@ -1088,8 +1151,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     __syncthreads();
     bf16x8 vring[PV_PF];
     bf16x8 pcur[2];
-    floatx16 s = qk_and_exp(it, kNoDma, false, none, vring, sprev, pcur);
-    pv_and_max(it, s, pcur, vring, kNoDma, none, [](int) {});
+    floatx16 s = qk_and_exp(it, kNoDma, false, none, vring, sprev, pcur, kR0, kWaits);
+    pv_and_max(it, s, pcur, vring, kNoDma, none, [](int) {}, kR0);
     sprev = s;
   }
   // Weights and output update of the last tile.
