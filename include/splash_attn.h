@@ -71,7 +71,11 @@ typedef struct splash_desc {
   int32_t page_size;         /* tokens per KV page: 16, 32, 64, 128 or 256 */
   int32_t max_pages_per_req; /* block_table row stride */
   int32_t num_pages;         /* pages in the pool (valid physical page ids are [0, num_pages)) */
-  int32_t num_splits;        /* split-KV chunks per request; 0 = library's choice (env SPLASH_NUM_SPLITS overrides) */
+  int32_t num_splits;        /* split-KV chunks per request (equal token ranges); 0 = library's choice
+                                (env SPLASH_NUM_SPLITS overrides).  While num_reqs x chunks x head
+                                groups is below the CU count, each of two or more chunks is
+                                computed by several workgroups over equal sub-ranges, and the
+                                merge combines them all; 1 always runs unsplit */
   float scale;               /* softmax scale applied to q.k, e.g. 1/sqrt(192) */
   int32_t num_kv_heads;      /* G latent KV heads per token (0 or 1: one); num_heads must be a multiple */
 } splash_desc;
@@ -200,7 +204,8 @@ int splash_release_workspace(void);
 
 /*
  * The launch plan splash_decode_attn would use for this share, without
- * launching anything (a pure host function): split-KV chunks per request,
+ * launching anything (a pure host function): split-KV partials per request
+ * (forced chunks times the workgroups computing each),
  * workgroups per (request, chunk) along the heads (over all KV heads the
  * share touches), and workspace bytes.
  * Returns the same validation status as splash_decode_attn.

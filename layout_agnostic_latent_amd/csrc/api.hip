@@ -192,6 +192,7 @@ struct Plan {
   int z_per_kv;         // head groups per KV head
   int grid_splits;      // split-KV chunks per request (grid mode: the blockIdx.x extent)
   int fixed_splits;     // > 0: every request cut into this many chunks
+  int fixed_sub;        // ... each computed by this many workgroups (equal sub-ranges)
   int chunk_tiles;      // otherwise: 32-token tiles per chunk
   // Stream mode: the decode kernel cuts the batch's tiles into at most
   // `target` equal ranges per head group (the grid's x extent) from the real
@@ -313,9 +314,22 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
   }
   const int64_t base = (int64_t)d->num_reqs * p->head_groups;
   if (forced > 0) {
+    // The caller's chunks; while two or more leave CUs idle (fewer
+    // workgroups than CUs), each chunk is computed by several workgroups
+    // over equal sub-ranges of its tiles, and the merge combines every
+    // sub-range.  One chunk (num_splits = 1) always runs unsplit.
+    int64_t sub = forced > 1 && base * forced > 0 ? kNumCUs / (base * forced) : 1;
+    if (const char* env = getenv("SPLASH_CHUNK_WORKGROUPS")) {
+      const int v = atoi(env);
+      if (v >= 1 && v <= 64) sub = v;
+    }
+    if (sub < 1) sub = 1;
+    if (max_tiles > 0 && sub > (max_tiles + forced - 1) / forced) sub = (max_tiles + forced - 1) / forced;
+    if (sub < 1) sub = 1;
     p->fixed_splits = forced;
+    p->fixed_sub = (int)sub;
     p->chunk_tiles = 0;
-    p->grid_splits = forced;
+    p->grid_splits = forced * sub <= 65535 ? (int)(forced * sub) : 65536;
   } else {
     // Aim for one round of about one workgroup per CU (each holds ~147 KiB
     // of LDS), with chunks of 4..128 tiles (128..4096 tokens): a chunk pays
@@ -327,6 +341,7 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
     if (chunk > kMaxChunkTiles) chunk = kMaxChunkTiles;
     if (max_tiles == 0) chunk = 1;
     p->fixed_splits = 0;
+    p->fixed_sub = 1;
     p->chunk_tiles = (int)chunk;
     p->grid_splits = max_tiles > 0 ? (int)((max_tiles + chunk - 1) / chunk) : 1;
   }
@@ -337,7 +352,7 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
   p->header = 0;
   // Longest run of tiles any one workgroup gets: forced splits cut each
   // request's tiles evenly, grid chunks are at most kMaxChunkTiles.
-  p->variant.max_chunk_tiles = forced > 0 ? (max_tiles + forced - 1) / forced
+  p->variant.max_chunk_tiles = forced > 0 ? ((max_tiles + forced - 1) / forced + p->fixed_sub - 1) / p->fixed_sub
                                           : (max_tiles < kMaxChunkTiles ? max_tiles : kMaxChunkTiles);
   const int64_t rows = (int64_t)d->num_reqs * hs;
   const int64_t groups = d->d_v / partial_group_cols(d->d_v, p->variant.wv);
@@ -430,6 +445,7 @@ int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, con
   a.tok_hi = tok_hi;
   a.num_reqs = desc->num_reqs;
   a.fixed_splits = p.fixed_splits;
+  a.fixed_sub = p.fixed_sub;
   a.chunk_tiles = p.chunk_tiles;
   a.scale_log2 = desc->scale * 1.4426950408889634f;
   a.out = out;

@@ -50,6 +50,7 @@ struct DecodeArgs {
   // b; every chunk is a partial when grid_partial, else the whole range goes
   // to the caller's output.
   int32_t fixed_splits;      // > 0: every request is cut into this many chunks
+  int32_t fixed_sub;         // fixed_splits > 0: workgroups per chunk, over equal sub-ranges of it
   int32_t chunk_tiles;       // fixed_splits == 0: 32-token tiles per chunk
   int32_t grid_partial;
   // Stream mode (plan_target > 0): the batch's tiles cut into equal ranges

@@ -1306,9 +1306,19 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
       if (hi > lo) {
         const int tf = lo / kTileTok;
         const int nt = (hi + kTileTok - 1) / kTileTok - tf;
-        const int chunk = a.fixed_splits > 0 ? (nt + a.fixed_splits - 1) / a.fixed_splits : a.chunk_tiles;
-        t_begin = tf + blockIdx.x * chunk;
-        t_end = min(t_begin + chunk, tf + nt);
+        if (a.fixed_splits > 0) {
+          // chunk blockIdx.x / fixed_sub of the request's fixed_splits equal
+          // chunks, sub-range blockIdx.x % fixed_sub of that chunk
+          const int chunk = (nt + a.fixed_splits - 1) / a.fixed_splits;
+          const int c = blockIdx.x / a.fixed_sub, k = blockIdx.x - c * a.fixed_sub;
+          const int cb = tf + c * chunk, ce = min(cb + chunk, tf + nt);
+          const int sub = ce > cb ? (ce - cb + a.fixed_sub - 1) / a.fixed_sub : 0;
+          t_begin = cb + k * sub;
+          t_end = min(t_begin + sub, ce);
+        } else {
+          t_begin = tf + blockIdx.x * a.chunk_tiles;
+          t_end = min(t_begin + a.chunk_tiles, tf + nt);
+        }
       }
       partial = a.grid_partial != 0;
       prow = ((int64_t)blockIdx.x * a.num_reqs + b) * a.n_heads;

@@ -90,7 +90,7 @@ def test_repack_rejects_bad_arguments(splash):
     assert L.splash_kv_repack(p, p, p, p, 1 << 20, 1 << 12, 16, 1, 1, None, None) == sp.EINVAL
 
 
-def test_plan_shapes(splash):
+def test_plan_shapes(splash, monkeypatch):
     # request-owned, 128 heads, 4,096 tokens: one head group, split to fill 256 CUs
     s, g, w = sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096)
     # unforced splits are cut on the device from the real lengths into at
@@ -103,8 +103,16 @@ def test_plan_shapes(splash):
     assert 512 * per_part + 16 * 16 <= w <= 512 * per_part + 1024
     # forced splits: fp16 outputs, then the records (each 256-byte aligned);
     # a 16-head slice stores 128-column groups
+    # 16 requests x 8 chunks leave 128 of 256 CUs idle: each chunk is
+    # computed by two workgroups, 16 partials per request
     s, g, w = sp.decode_plan(16, 128, 576, 512, 64, 256, 4096, 0.07, 0, 16, 0, 16384, num_splits=8)
-    assert s == 8 and g == 1 and w == 8 * 16 * 16 * 512 * 2 + 4 * 8 * 16 * 16 * 8
+    assert s == 16 and g == 1 and w == 16 * 16 * 16 * 512 * 2 + 4 * 16 * 16 * 16 * 8
+    monkeypatch.setenv("SPLASH_CHUNK_WORKGROUPS", "1")
+    s, g, w = sp.decode_plan(16, 128, 576, 512, 64, 256, 4096, 0.07, 0, 16, 0, 16384, num_splits=8)
+    assert s == 8 and w == 8 * 16 * 16 * 512 * 2 + 4 * 8 * 16 * 16 * 8
+    monkeypatch.delenv("SPLASH_CHUNK_WORKGROUPS")
+    # no more workgroups per chunk than the chunk has tiles (2 tiles each here)
+    assert sp.decode_plan(1, 128, 576, 512, 64, 256, 4096, 0.07, 0, 16, 0, 512, num_splits=8)[0] == 16
     # a 64-head slice uses 32-head x 2 waves groups
     s, g, _ = sp.decode_plan(2, 128, 576, 512, 64, 8, 16, 0.07, 0, 64, 0, 512)
     assert g == 1
@@ -141,6 +149,9 @@ def test_plan_kv_heads(splash):
 
 def test_plan_env_override(splash, monkeypatch):
     monkeypatch.setenv("SPLASH_NUM_SPLITS", "5")
+    # 16 requests x 5 chunks = 80 workgroups: three per chunk fill 240 CUs
+    assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096)[0] == 15
+    monkeypatch.setenv("SPLASH_CHUNK_WORKGROUPS", "1")
     assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096)[0] == 5
     # an explicit num_splits in the descriptor wins
     assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_splits=3)[0] == 3
