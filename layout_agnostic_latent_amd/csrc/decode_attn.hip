@@ -694,7 +694,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
                      auto waits) -> floatx16 {
     constexpr int R = decltype(reg)::value;
     constexpr bool W = decltype(waits)::value || C::KSPLIT;  // the score exchange reads them at once
-    const char* tile = smem + (it % C::NBUF) * C::TILE_B;
+    const char* tile = smem + (it & (C::NBUF - 1)) * C::TILE_B;
     constexpr int PF = C::KPF < C::KSW ? C::KPF : C::KSW;
     floatx16 sacc;
     bf16x8 kring[PF];
@@ -777,7 +777,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   constexpr int NM = C::NM;
   constexpr int PV_PF = C::VPF;
   auto vread = [&](int it, int i) -> bf16x8 {
-    const char* tile = smem + (it % C::NBUF) * C::TILE_B;
+    const char* tile = smem + (it & (C::NBUF - 1)) * C::TILE_B;
     const int ks = i / C::VB, vb = i % C::VB;
     const char* v0 = tile + vaddr(0, ks, vb);
     const char* v1 = tile + vaddr(1, ks, vb);
@@ -860,6 +860,12 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // weights are first consumed by its PV products, which come after these
   // score MFMAs.  Returns tile j's scores and tile j-1's packed weights; the
   // sums of tile j-1's weights are added to the running sums.
+  // Main-loop iterations alternate the score chain between the two register
+  // blocks (kAltChains): tile j's scores stay in their block while tile
+  // j+1's chain accumulates in the other, and the chain's wait states are
+  // left to the PV steps before the first slice that reads the scores.
+  constexpr bool kAltChains = TBL && !C::KSPLIT && C::NM >= 16;
+  constexpr int kSlice0 = kAltChains ? 6 : 0;
   auto qk_and_exp = [&](int it, auto with_dma, bool do_dma, const DmaPlan& dp, bf16x8 (&vring)[PV_PF],
                         floatx16& sprev, bf16x8 (&pcur)[2], auto reg, auto waits) -> floatx16 {
     uint32_t pw[2][4];
@@ -870,6 +876,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
       vpf(sidx);
       const int t = sidx - kExpStep0;
       if (t >= 0 && t < kExpSlices) exp_slice(t, sprev, m, pw, lsum, lrsum);
+      // the previous tile's scores keep the other block (no copy of them)
+      if constexpr (kAltChains && decltype(with_dma)::value) chain_hold<1 - decltype(reg)::value>(sprev);
     }, reg, waits);
 #pragma unroll
     for (int t = C::KSW - kExpStep0; t < kExpSlices; ++t) exp_slice(t, sprev, m, pw, lsum, lrsum);
@@ -889,8 +897,6 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // With the main loop's chains (no wait states of their own) the first
   // slice reading the scores comes after kSlice0 PV steps of at least four
   // instructions each.
-  constexpr bool kAltChains = TBL && !C::KSPLIT && C::NM >= 16;  // alternating chains, no chain wait states
-  constexpr int kSlice0 = kAltChains ? 6 : 0;
   auto pv_and_max = [&](int it, floatx16& s, const bf16x8 (&pcur)[2], bf16x8 (&vring)[PV_PF], auto with_dma,
                         const DmaPlan& dp, auto&& extra, auto reg) {
     // tiles of the main loop (with_dma) lie strictly inside the chunk: only
@@ -915,9 +921,10 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
       }
       const int j = decltype(with_dma)::value ? i - kSlice0 : i;  // slice of this step
       if constexpr (kAltChains && decltype(with_dma)::value) {
-        // the scores stay in the chain's registers until the wait states
-        // are covered (the PV steps before this one)
-        if (j == 0) chain_hold<decltype(reg)::value>(s);
+        // the scores stay in the chain's registers: until the wait states
+        // are covered (the PV steps before slice 0), and on into the next
+        // tile's exponentials
+        if (j >= 0) chain_hold<decltype(reg)::value>(s);
       }
       if (j == 0) {
         mx[0] = max3(s[0], s[1], s[2]);
@@ -1121,9 +1128,9 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     pv_and_max(it, s, pcur, vring, kDma, dp, [&](int i) {
       if constexpr (TBL) {
         if (i == kTblLoadStep && tn < t_end) entry = tbl[it + 3];
-        if (i == kPlanStep && tn < t_end) dp_next = tbl_plan(entry, it + 3, (it + 3) % C::NBUF);
+        if (i == kPlanStep && tn < t_end) dp_next = tbl_plan(entry, it + 3, (it + 3) & (C::NBUF - 1));
       } else {
-        if (i == kPlanStep && tn < t_end) dp_next = dma_plan(tn, (it + 3) % C::NBUF, pages_of(tn));
+        if (i == kPlanStep && tn < t_end) dp_next = dma_plan(tn, (it + 3) & (C::NBUF - 1), pages_of(tn));
       }
     }, reg);
     dp = dp_next;
