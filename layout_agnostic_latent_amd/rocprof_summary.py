@@ -114,18 +114,24 @@ def counters_main(argv) -> None:
     ap.add_argument("--counters", action="store_true")
     ap.add_argument("--name", required=True)
     ap.add_argument("--command", required=True, action="append")
-    ap.add_argument("--run", required=True, action="append", nargs=3, metavar=("LABEL", "DIR", "ALG_FLOPS"),
-                    help="workload label, rocprofv3 output directory, algorithmic FLOPs per decode call")
+    ap.add_argument("--run", required=True, action="append", nargs=3, metavar=("LABEL", "DIRS", "ALG_FLOPS"),
+                    help="workload label, rocprofv3 output directories (comma-separated passes of one "
+                         "workload), algorithmic FLOPs per decode call")
+    ap.add_argument("--transpose", action="store_true",
+                    help="one row per counter (with its value per wave), one column per workload")
     args = ap.parse_args(argv)
     rows = []
-    for label, d, alg in args.run:
+    for label, dirs, alg in args.run:
         vals = defaultdict(list)
-        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            for row in csv.DictReader(open(f)):
-                if "decode_attn_kernel" in row["Kernel_Name"]:
-                    vals[row["Counter_Name"]].append(float(row["Counter_Value"]))
+        for d in dirs.split(","):
+            for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+                for row in csv.DictReader(open(f)):
+                    if "decode_attn_kernel" in row["Kernel_Name"]:
+                        vals[row["Counter_Name"]].append(float(row["Counter_Value"]))
         rows.append((label, float(alg), {k: statistics.mean(v) for k, v in vals.items()}))
     names = sorted({k for _, _, v in rows for k in v})
+    if args.transpose:
+        return _transposed(args, rows, names)
     lines = [f"# {args.name}", "", "Produced by:", ""] + [f"    {c}" for c in args.command]
     lines += ["", f"Kernel source hash: `{kernel_source_hash()}`", "",
               "Per decode_attn_kernel dispatch (average over the run's dispatches):", "",
@@ -140,6 +146,28 @@ def counters_main(argv) -> None:
                      f"{'' if share is None else f'{100 * share:.2f}%'} |")
     lines += ["", "MfmaUtil: MFMA busy cycles over (active cycles x SIMDs), percent. MfmaFlopsBF16: 512 x the "
               "bf16 MFMA op count. LDS conflict share: bank-conflict cycles over conflict-free LDS cycles."]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, args.name + ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _transposed(args, rows, names) -> None:
+    """Counter-per-row table: each workload's per-dispatch average and that
+    divided by SQ_WAVES (a per-wave figure; the SQ cycle counters count
+    4-cycle units)."""
+    lines = [f"# {args.name}", "", "Produced by:", ""] + [f"    {c}" for c in args.command]
+    lines += ["", f"Kernel source hash: `{kernel_source_hash()}`", "",
+              "Per decode_attn_kernel dispatch (average over the run's dispatches), and per wave:", "",
+              "| counter | " + " | ".join(f"{label} | per wave" for label, _, _ in rows) + " |",
+              "|---|" + "---|---|" * len(rows)]
+    for n in names:
+        cells = []
+        for _, _, v in rows:
+            w = v.get("SQ_WAVES")
+            cells.append(f"{v[n]:.6g}" if n in v else "")
+            cells.append(f"{v[n] / w:.6g}" if n in v and w else "")
+        lines.append(f"| {n} | " + " | ".join(cells) + " |")
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, args.name + ".md"), "w") as f:
         f.write("\n".join(lines) + "\n")
