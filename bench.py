@@ -205,7 +205,7 @@ def main():
         parts["lse_merge_us"] = round(lse_merge_us, 2)
         parts["lse_merge_TBps"] = round(mb / (lse_merge_us * 1e-6) / 1e12, 3)
 
-    traffic = measured_traffic(args.workload, "decode_attn_kernel")
+    traffic = measured_traffic(args.workload, "decode_attn")
 
     # Peaks of this GPU as measured (after the timed regions): the fractions
     # above use the published peaks; these say what the chip sustains.

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libsplash_attn.so")
-SOURCES = ["api.hip", "decode_attn.hip", "lse_merge.hip", "kv_repack.hip", "peaks.hip"]
+SOURCES = ["api.hip", "decode_attn.hip", "decode_attn16.hip", "lse_merge.hip", "kv_repack.hip", "peaks.hip"]
 ARCH = "gfx950"
 
 

@@ -186,7 +186,7 @@ int page_shift_of(int ps) {
 struct Plan {
   DecodeVariant variant;
   int head_groups;      // workgroups along the heads (KV heads touched x z_per_kv)
-  int heads_per_group;  // 32 * wh
+  int heads_per_group;  // head_tile * wh
   int kv_group;         // query heads per KV head
   int kv_first;         // first KV head the share touches
   int z_per_kv;         // head groups per KV head
@@ -280,19 +280,22 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
   // Heads per workgroup: 32 (4 waves split the V columns), 64 (2 head
   // groups x 2 column halves) or 128 (4 head groups).  SPLASH_WG_HEADS
   // overrides the choice (tuning).
-  int wg_heads = slice <= 32 ? 32 : (slice <= 64 ? 64 : 128);
+  const bool latent = d->d_qk == 576 && d->d_v == 512;
+  int wg_heads = slice <= 16 && latent ? 16 : (slice <= 32 ? 32 : (slice <= 64 ? 64 : 128));
   if (const char* env = getenv("SPLASH_WG_HEADS")) {
     const int v = atoi(env);
-    if (v == 32 || v == 64 || v == 128) wg_heads = v;
+    if ((v == 16 && latent) || v == 32 || v == 64 || v == 128) wg_heads = v;
   }
-  if (wg_heads == 32) {
-    p->variant = {d->d_qk, d->d_v, 1, wv_max, 0};
+  if (wg_heads == 16) {
+    p->variant = {d->d_qk, d->d_v, 1, 4, 0, 16};
+  } else if (wg_heads == 32) {
+    p->variant = {d->d_qk, d->d_v, 1, wv_max, 0, 32};
   } else if (wg_heads == 64 && d->d_v / 32 >= 2 && d->d_qk == 576) {
-    p->variant = {d->d_qk, d->d_v, 2, 2, 0};
+    p->variant = {d->d_qk, d->d_v, 2, 2, 0, 32};
   } else {
-    p->variant = {d->d_qk, d->d_v, 4, 1, 0};
+    p->variant = {d->d_qk, d->d_v, 4, 1, 0, 32};
   }
-  p->heads_per_group = 32 * p->variant.wh;
+  p->heads_per_group = p->variant.head_tile * p->variant.wh;
   p->kv_group = group;
   p->kv_first = kv_first;
   p->z_per_kv = (slice + p->heads_per_group - 1) / p->heads_per_group;

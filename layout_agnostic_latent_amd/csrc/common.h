@@ -78,6 +78,7 @@ constexpr int32_t kStreamEmpty = 2;
 struct DecodeVariant {
   int d_qk, d_v, wh, wv;
   int64_t max_chunk_tiles;
+  int head_tile;  // heads per MFMA tile: 32 (32x32x16 kernel) or 16 (16x16x32 kernel, wh = 1, wv = 4)
 };
 
 // Records `msg` as the thread's last error (splash_last_error) and returns
@@ -86,6 +87,8 @@ int report_error(int code, const char* msg);
 
 // Each launcher takes two optional events that, when non-null, record the
 // start and end of the kernel itself (hipExtLaunchKernelGGL), for profiling.
+hipError_t launch_decode16(const DecodeVariant& v, dim3 grid, const DecodeArgs& a, hipStream_t stream,
+                           hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_decode(const DecodeVariant& v, dim3 grid, const DecodeArgs& a, hipStream_t stream,
                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 

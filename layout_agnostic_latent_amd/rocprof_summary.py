@@ -64,7 +64,7 @@ def kernel_source_hash() -> str:
     """Hash of the kernel sources' code (not their comments), recorded with the
     counter runs: bench.py uses a record only while the hash still matches."""
     h = hashlib.sha256()
-    for f in ("decode_attn.hip", "lse_merge.hip", "kv_repack.hip", "common.h"):
+    for f in ("decode_attn.hip", "decode_attn16.hip", "decode_device.h", "lse_merge.hip", "kv_repack.hip", "common.h"):
         with open(os.path.join(PKG, "csrc", f), encoding="utf-8") as fh:
             h.update(_code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
@@ -77,11 +77,12 @@ def short(name: str) -> str:
         if "<float" in name or "split_merge_kernelIf" in name:
             return "split_merge_kernel<fp32> (splash_lse_merge)"
         return "split_merge_kernel<fp16> (split-KV merge)"
-    for key in ("decode_attn_kernel", "lse_merge_kernel", "kv_repack_kernel", "mfma_peak_kernel", "read_peak_kernel"):
+    for key in ("decode_attn_kernel", "decode_attn16_kernel", "lse_merge_kernel", "kv_repack_kernel",
+                "mfma_peak_kernel", "read_peak_kernel"):
         if key in name:
             i = name.find("<")
             j = name.find(">", i)
-            return key + (name[i:j + 1] if key == "decode_attn_kernel" and i >= 0 else "")
+            return key + (name[i:j + 1] if key.startswith("decode_attn") and i >= 0 else "")
     return name.split("(")[0][:60]
 
 
@@ -126,7 +127,7 @@ def counters_main(argv) -> None:
         for d in dirs.split(","):
             for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
                 for row in csv.DictReader(open(f)):
-                    if "decode_attn_kernel" in row["Kernel_Name"]:
+                    if "decode_attn" in row["Kernel_Name"]:
                         vals[row["Counter_Name"]].append(float(row["Counter_Value"]))
         rows.append((label, float(alg), {k: statistics.mean(v) for k, v in vals.items()}))
     names = sorted({k for _, _, v in rows for k in v})
@@ -134,7 +135,7 @@ def counters_main(argv) -> None:
         return _transposed(args, rows, names)
     lines = [f"# {args.name}", "", "Produced by:", ""] + [f"    {c}" for c in args.command]
     lines += ["", f"Kernel source hash: `{kernel_source_hash()}`", "",
-              "Per decode_attn_kernel dispatch (average over the run's dispatches):", "",
+              "Per decode-kernel dispatch (average over the run's dispatches):", "",
               "| workload | " + " | ".join(names) + " | MFMA FLOPs / algorithmic | LDS conflict share |",
               "|---|" + "---|" * (len(names) + 2)]
     for label, alg, v in rows:
@@ -158,7 +159,7 @@ def _transposed(args, rows, names) -> None:
     4-cycle units)."""
     lines = [f"# {args.name}", "", "Produced by:", ""] + [f"    {c}" for c in args.command]
     lines += ["", f"Kernel source hash: `{kernel_source_hash()}`", "",
-              "Per decode_attn_kernel dispatch (average over the run's dispatches), and per wave:", "",
+              "Per decode-kernel dispatch (average over the run's dispatches), and per wave:", "",
               "| counter | " + " | ".join(f"{label} | per wave" for label, _, _ in rows) + " |",
               "|---|" + "---|---|" * len(rows)]
     for n in names:

@@ -31,3 +31,5 @@ def test_summariser_names_the_two_merges_apart():
     assert rs.short(fp32).startswith("split_merge_kernel<fp32>")
     dec = "void splash::(anonymous namespace)::decode_attn_kernel<576, 512, 4, 1>(splash::DecodeArgs)"
     assert rs.short(dec) == "decode_attn_kernel<576, 512, 4, 1>"
+    dec16 = "void splash::(anonymous namespace)::decode_attn16_kernel<576, 512>(splash::DecodeArgs)"
+    assert rs.short(dec16) == "decode_attn16_kernel<576, 512>"
