@@ -414,6 +414,47 @@ def test_page16_range_starting_mid_tile(tok_lo):
         assert_close(go, gl, ro, rl, what=f"page 16, tok_lo {tok_lo}, splits {splits}")
 
 
+@pytest.mark.parametrize("ps", [16, 64, 256])
+def test_head16_tile_pages_ranges_and_groups(ps):
+    """Shares of at most 16 heads run on the 16x16x32 tile: page sizes 16 to
+    256; a token range starting in the second half of a 32-token tile with
+    the block-table entries before it -1 (never read: the autouse fixture
+    checks that no bad-page bit is set); full, partial (8 and 12 heads) and
+    KV-head-crossing head groups; unsplit, forced and planned splits."""
+    tok_lo = 48 if ps == 16 else 3 * ps // 2
+    c = W.make_decode_case("h16", 47 + ps, [700, 1, 129, 300, 1000], num_heads=128, d_qk=576, d_v=512,
+                           page_size=ps, scale=W.LATENT_SCALE, tok_lo=tok_lo, tok_hi=900,
+                           live_only_in_range=True, extra_pages=2)
+    bt = c.block_table.copy()
+    bt[:, :tok_lo // ps] = -1
+    c2 = W.DecodeCase(**{**c.__dict__, "block_table": bt})
+    t = to_dev(c2)
+    for heads in ((16, 32), (120, 128), (3, 15)):
+        ro, rl = run_oracle(c2, head_lo=heads[0], head_hi=heads[1])
+        for splits in (0, 1, 3):
+            _print(f"case head16 ps={ps} heads={heads} splits={splits}")
+            go, gl = run_decode(c2, t, head_lo=heads[0], head_hi=heads[1], num_splits=splits)
+            assert_close(go, gl, ro, rl, what=f"16-head tile, page {ps}, heads {heads}, splits {splits}")
+
+
+def test_head16_tile_rescale():
+    """Growing scores on the 16-head tile: the running max moves many times
+    (rope dims only, so the output keeps its scale)."""
+    c = W.make_decode_case("grow16", 48, [4096, 2500], num_heads=128, d_qk=576, d_v=512, page_size=64,
+                           scale=W.LATENT_SCALE)
+    for b in range(c.num_reqs):
+        n = int(c.seq_lens[b])
+        for tkn in range(n):
+            p, s = c.block_table[b, tkn // 64], tkn % 64
+            rope = (c.kv_pages[p, s, c.d_v:].astype(np.uint32) << 16).view(np.float32) * (1.0 + tkn / 64.0)
+            c.kv_pages[p, s, c.d_v:] = W.bf16_bits(rope)
+    for splits in (0, 1):
+        _print(f"case head16 growing scores splits={splits}")
+        go, gl = run_decode(c, head_lo=32, head_hi=48, num_splits=splits)
+        ro, rl = run_oracle(c, head_lo=32, head_hi=48)
+        assert_close(go, gl, ro, rl, what=f"16-head tile, growing scores, splits {splits}")
+
+
 @pytest.mark.parametrize("ps", [16, 32, 128, 256])
 def test_other_page_sizes(ps):
     c = W.make_decode_case("pages", 42, [700, 1, 129, 300], num_heads=40, d_qk=576, d_v=512, page_size=ps,
