@@ -363,6 +363,22 @@ def test_many_ragged_requests():
     assert_close(go, gl, ro, rl, what="many ragged")
 
 
+@pytest.mark.parametrize("heads", [(0, 128), (48, 64)])
+def test_more_than_64_ragged_latent_requests(heads):
+    """100 ragged 576-dim requests: the plan is made by the workgroup, not by
+    each wave (which covers at most 64 requests), for the 128-head tile and
+    for the 16-head tile."""
+    rng = np.random.default_rng(78)
+    lens = rng.integers(0, 3001, size=100)
+    lens[::17] = 0
+    c = W.make_decode_case("many576", 49, lens, num_heads=128, d_qk=576, d_v=512, page_size=64,
+                           scale=W.LATENT_SCALE, head_lo=heads[0], head_hi=heads[1])
+    _print(f"case 100 ragged latent requests heads={heads}")
+    go, gl = run_decode(c)
+    ro, rl = run_oracle(c)
+    assert_close(go, gl, ro, rl, what=f"100 ragged latent requests, heads {heads}")
+
+
 def test_one_long_request_many_chunks():
     """A 150,000-token request next to a short and an empty one: about 250
     device-planned chunks of one request, merged by its own part list."""
@@ -482,13 +498,17 @@ def test_large_scores_rescale():
     assert_close(go, gl, ro, rl, what="growing scores")
 
 
-def test_bad_page_index_is_flagged_not_faulted():
-    """A block-table entry outside the pool is read as page 0 and raises the device error bit."""
-    c = W.make_decode_case("bad", 44, [130], num_heads=32, d_qk=576, d_v=512, page_size=64,
-                           scale=W.LATENT_SCALE)
+@pytest.mark.parametrize("heads", [16, 32, 128])
+def test_bad_page_index_is_flagged_not_faulted(heads):
+    """A block-table entry outside the pool is read as page 0 and raises the
+    device error bit: the 16-head tile, the 32-head one, and the 128-head one
+    (whose tile-address table checks the entries in its prologue)."""
+    c = W.make_decode_case("bad", 44, [130], num_heads=128, d_qk=576, d_v=512, page_size=64,
+                           scale=W.LATENT_SCALE, head_hi=heads)
     bt = c.block_table.copy()
     bt[0, 1] = c.num_pages + 1000
     c2 = W.DecodeCase(**{**c.__dict__, "block_table": bt})
+    _print(f"case bad page heads={heads}")
     run_decode(c2)
     assert sp.device_errors(clear=True) & sp.DEVERR_BAD_PAGE
 
