@@ -341,17 +341,21 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   auto issue_one = [&](const DmaPlan& d, int i) {
     if constexpr (TBL) {
       // one 64-bit base for the wave's nine instructions (immediate offsets);
-      // instruction i fills slab i of the wave's rows, at d.lds + i * SLAB_B
+      // instruction i fills slab i of the wave's rows, at d.lds + i * SLAB_B.
+      // The slot address is re-read here so that each instruction's m0 is
+      // computed in its own MFMA gap, not all in one.
+      uint32_t l = __builtin_amdgcn_readfirstlane(d.lds);
+      asm volatile("" : "+s"(l));
       switch (i) {
-        case 0: lds_dma16_imm<0>(d.wbase, d.voff, d.lds + 0 * C::SLAB_B); break;
-        case 1: lds_dma16_imm<1>(d.wbase, d.voff, d.lds + 1 * C::SLAB_B); break;
-        case 2: lds_dma16_imm<2>(d.wbase, d.voff, d.lds + 2 * C::SLAB_B); break;
-        case 3: lds_dma16_imm<3>(d.wbase, d.voff, d.lds + 3 * C::SLAB_B); break;
-        case 4: lds_dma16_imm<4>(d.wbase, d.voff, d.lds + 4 * C::SLAB_B); break;
-        case 5: lds_dma16_imm<5>(d.wbase, d.voff, d.lds + 5 * C::SLAB_B); break;
-        case 6: lds_dma16_imm<6>(d.wbase, d.voff, d.lds + 6 * C::SLAB_B); break;
-        case 7: lds_dma16_imm<7>(d.wbase, d.voff, d.lds + 7 * C::SLAB_B); break;
-        default: lds_dma16_imm<8>(d.wbase, d.voff, d.lds + 8 * C::SLAB_B); break;
+        case 0: lds_dma16_imm<0>(d.wbase, d.voff, l + 0 * C::SLAB_B); break;
+        case 1: lds_dma16_imm<1>(d.wbase, d.voff, l + 1 * C::SLAB_B); break;
+        case 2: lds_dma16_imm<2>(d.wbase, d.voff, l + 2 * C::SLAB_B); break;
+        case 3: lds_dma16_imm<3>(d.wbase, d.voff, l + 3 * C::SLAB_B); break;
+        case 4: lds_dma16_imm<4>(d.wbase, d.voff, l + 4 * C::SLAB_B); break;
+        case 5: lds_dma16_imm<5>(d.wbase, d.voff, l + 5 * C::SLAB_B); break;
+        case 6: lds_dma16_imm<6>(d.wbase, d.voff, l + 6 * C::SLAB_B); break;
+        case 7: lds_dma16_imm<7>(d.wbase, d.voff, l + 7 * C::SLAB_B); break;
+        default: lds_dma16_imm<8>(d.wbase, d.voff, l + 8 * C::SLAB_B); break;
       }
       return;
     }
@@ -379,17 +383,25 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   uint32_t* const tbl = (uint32_t*)(smem + C::BODY_B) + (TBL ? wave * kTblTiles : 0);
   const uint32_t chunk_off = 16u * ((uint32_t)(lane & 7) ^ row_swizzle(8 * wave + l8));
   const uint32_t voff_int = (uint32_t)(l8 * row_b) + chunk_off;
-  auto tbl_plan = [&](uint32_t entry, int i, int slot) -> DmaPlan {
+  // The plan of an interior tile, and the lane offset of an edge tile (the
+  // first or the last of the segment; the main loop takes the two apart so
+  // that each fits one MFMA gap).
+  auto tbl_plan_interior = [&](uint32_t entry, int slot) -> DmaPlan {
     DmaPlan d{};
-    d.wbase = (const char*)kv + ((uint64_t)__builtin_amdgcn_readfirstlane(entry) << 7);
+    d.wbase = (const char*)kv + ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(entry) << 7);
     d.lds = smem_base + slot * C::TILE_B + wave * 1024;
     d.voff = voff_int;
-    if (i == 0 || i == ntiles - 1) {
-      const int tokg = (t_begin + i) * kTileTok + 8 * wave;
-      const int tokw = min(max(tokg, mlo), mhi - 1);
-      const int row = min(max(tokg + l8, mlo), mhi - 1);
-      d.voff = (uint32_t)((row - tokw) * row_b) + chunk_off;
-    }
+    return d;
+  };
+  auto tbl_edge_voff = [&](int i) -> uint32_t {
+    const int tokg = (t_begin + i) * kTileTok + 8 * wave;
+    const int tokw = min(max(tokg, mlo), mhi - 1);
+    const int row = min(max(tokg + l8, mlo), mhi - 1);
+    return (uint32_t)((row - tokw) * row_b) + chunk_off;
+  };
+  auto tbl_plan = [&](uint32_t entry, int i, int slot) -> DmaPlan {
+    DmaPlan d = tbl_plan_interior(entry, slot);
+    if (i == 0 || i == ntiles - 1) d.voff = tbl_edge_voff(i);
     return d;
   };
 
@@ -632,23 +644,100 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // left to the PV steps before the first slice that reads the scores.
   constexpr bool kAltChains = TBL && !C::KSPLIT && C::NM >= 16;
   constexpr int kSlice0 = kAltChains ? 6 : 0;
+  // The main loop's exponentials spread over all 36 score MFMAs.  The wave
+  // issues one instruction per 4-cycle slot and an MFMA occupies the matrix
+  // core for 8, so the 7 slots after each MFMA are free for other work; a
+  // gap with more delays the next MFMA.  A gap holds a K read and its wait
+  // (2 slots), every fourth (steps 0, 4, .., 32) also a DMA (3 more).  An
+  // exp2 takes 4 slots and one wait state before its result is read (5), and
+  // one before it may read a value the VALU just wrote, so each goes alone
+  // into an odd gap, its exponent one gap earlier:
+  //   step 0:      exponent of element 0;
+  //   step 4m+1:   exp2 of element 2m;   step 4m+3: exp2 of element 2m+1;
+  //   step 4m+2:   sum of element 2m, exponents of elements 2m+1 and 2m+2,
+  //                rounded sum of pair m-1;
+  //   step 4m+4:   sum of element 2m+1, bf16 packing of pair m (m < 7);
+  //   steps 32-35: the last sum, packing and rounded sum, then the running
+  //   sums (each value is used at least one MFMA after it is made).
+  constexpr bool kSpreadExp = kAltChains && C::KSW == 36 && C::DMA_QK == 9 && C::KPF == 4 && PV_PF == 4;
+  auto exp_spread = [&](int st, floatx16& sp, float m, uint32_t (&pw)[2][4], float& lsum, float& lrsum) {
+    auto expo = [&](int e) {
+      float x = __builtin_fmaf(sp[e], a.scale_log2, -m);
+      pin(x);
+      sp[e] = x;
+    };
+    auto ex2 = [&](int e) {
+      float x = __builtin_amdgcn_exp2f(sp[e]);
+      pin(x);
+      sp[e] = x;
+    };
+    auto add = [&](int e) {
+      lsum += sp[e];
+      pin(lsum);
+    };
+    auto pack = [&](int k) {
+      const bf16x2 pair = {(__bf16)sp[2 * k], (__bf16)sp[2 * k + 1]};
+      uint32_t w = __builtin_bit_cast(uint32_t, pair);
+      asm volatile("" : "+v"(w));
+      pw[k >> 2][k & 3] = w;
+    };
+    auto rsum = [&](int k) {
+      lrsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[k >> 2][k & 3]), ones, lrsum, false);
+      pin(lrsum);
+    };
+    if (st == 0) {
+      expo(0);
+    } else if (st <= 31) {
+      const int mm = (st - 1) >> 2, r = (st - 1) & 3;
+      if (r == 0) {
+        ex2(2 * mm);
+      } else if (r == 1) {
+        add(2 * mm);
+        expo(2 * mm + 1);
+        if (mm < 7) expo(2 * mm + 2);
+        if (mm >= 1) rsum(mm - 1);
+      } else if (r == 2) {
+        ex2(2 * mm + 1);
+      } else {
+        add(2 * mm + 1);
+        pack(mm);
+      }
+    } else if (st == 32) {
+      add(15);
+    } else if (st == 33) {
+      pack(7);
+    } else if (st == 34) {
+      rsum(7);
+    }
+  };
   auto qk_and_exp = [&](int it, auto with_dma, bool do_dma, const DmaPlan& dp, bf16x8 (&vring)[PV_PF],
                         floatx16& sprev, bf16x8 (&pcur)[2], auto reg, auto waits) -> floatx16 {
+    constexpr bool spread = kSpreadExp && decltype(with_dma)::value;
     uint32_t pw[2][4];
     float lsum = 0.0f, lrsum = 0.0f;
     const float m = m_run;
     auto vpf = vprefetch_hook(it - 1, vring);
     floatx16 s = qk_tile(it, with_dma, do_dma, dp, [&](int sidx) {
       vpf(sidx);
-      const int t = sidx - kExpStep0;
-      if (t >= 0 && t < kExpSlices) exp_slice(t, sprev, m, pw, lsum, lrsum);
+      if constexpr (spread) {
+        exp_spread(sidx, sprev, m, pw, lsum, lrsum);
+        if (sidx == 35) {
+          l_run += lsum;
+          lr_run += lrsum;
+        }
+      } else {
+        const int t = sidx - kExpStep0;
+        if (t >= 0 && t < kExpSlices) exp_slice(t, sprev, m, pw, lsum, lrsum);
+      }
       // the previous tile's scores keep the other block (no copy of them)
       if constexpr (kAltChains && decltype(with_dma)::value) chain_hold<1 - decltype(reg)::value>(sprev);
     }, reg, waits);
+    if constexpr (!spread) {
 #pragma unroll
-    for (int t = C::KSW - kExpStep0; t < kExpSlices; ++t) exp_slice(t, sprev, m, pw, lsum, lrsum);
-    l_run += lsum;
-    lr_run += lrsum;
+      for (int t = C::KSW - kExpStep0; t < kExpSlices; ++t) exp_slice(t, sprev, m, pw, lsum, lrsum);
+      l_run += lsum;
+      lr_run += lrsum;
+    }
     pack_probs(pw, pcur);
     return s;
   };
@@ -726,7 +815,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     };
     pv_tile(it - 1, pcur, vring, step);
     // slices beyond the MFMA count (variants with fewer V blocks)
-    constexpr int kSteps = 10 + kSlice0 > kPlanStep + 1 ? 10 + kSlice0 : kPlanStep + 1;
+    constexpr int kSteps = 10 + kSlice0 > kPlanStep + 3 ? 10 + kSlice0 : kPlanStep + 3;
 #pragma unroll
     for (int i = C::NM; i < kSteps; ++i) step(i);
     const bool any_need = __any(need);
@@ -883,6 +972,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // One pipelined tile: the exponentials of `prev` under the tile's score
   // chain, then its PV steps; returns the tile's scores.
   auto iteration = [&](floatx16& prev, auto reg, auto waits) -> floatx16 {
+    constexpr int R = decltype(reg)::value;
+    if constexpr (kAltChains) chain_hold<1 - R>(prev);  // no home of its own between tiles
     wait_vmcnt<C::DMA_W>();
     __syncthreads();
     bf16x8 vring[PV_PF];
@@ -893,12 +984,15 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     uint32_t entry = 0;  // table entry of tile it + 3 (TBL), read early, used at the plan step
     pv_and_max(it, s, pcur, vring, kDma, dp, [&](int i) {
       if constexpr (TBL) {
+        // tile it + 3 >= 3 is the segment's first tile never, its last one at most once
         if (i == kTblLoadStep && tn < t_end) entry = tbl[it + 3];
-        if (i == kPlanStep && tn < t_end) dp_next = tbl_plan(entry, it + 3, (it + 3) & (C::NBUF - 1));
+        if (i == kPlanStep && tn < t_end) dp_next = tbl_plan_interior(entry, (it + 3) & (C::NBUF - 1));
+        if (i == kPlanStep + 2 && tn == t_end - 1) dp_next.voff = tbl_edge_voff(it + 3);
       } else {
         if (i == kPlanStep && tn < t_end) dp_next = dma_plan(tn, (it + 3) & (C::NBUF - 1), pages_of(tn));
       }
     }, reg);
+    if constexpr (kAltChains) chain_hold<R>(s);
     dp = dp_next;
     return s;
   };
