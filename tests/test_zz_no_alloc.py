@@ -59,3 +59,16 @@ def test_noalloc_forced_splits_and_unsplit():
     (ro, rl), (go, gl) = _both(tiny)
     assert_close(go, gl, ro, rl, what="noalloc vs decode_attn, tiny")
     assert sp.device_errors(clear=True) == 0
+
+
+def test_noalloc_16_head_tile():
+    """A 16-head share (the 16x16x32 tile) through the allocation-free entry
+    point, planned and forced splits."""
+    sp.device_errors(clear=True)
+    case = W.make_decode_case("noalloc_h16", 48, [3000, 700, 65, 1800], num_heads=128, d_qk=576, d_v=512,
+                              page_size=64, scale=W.LATENT_SCALE, head_lo=16, head_hi=32)
+    for splits in (0, 3):
+        print(f"case noalloc 16-head tile splits={splits}", flush=True)
+        (ro, rl), (go, gl) = _both(case, num_splits=splits)
+        assert_close(go, gl, ro, rl, what=f"noalloc vs decode_attn, 16-head tile, splits={splits}")
+    assert sp.device_errors(clear=True) == 0
