@@ -252,7 +252,9 @@ def main():
                            + (" + kv_repack(half of the requests)" if rep is not None else "")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_attn_kernel"},
+                     "kernel": "decode_attn16_kernel" if case.d_qk == 576 and min(Hs, case.q.shape[1]
+                                                                                   // case.num_kv_heads) <= 16
+                     else "decode_attn_kernel"},
         "parts": parts,
         "measured_peaks": peaks,
         "cpu_baseline": cpu,
