@@ -9,12 +9,14 @@
 // heads), and V is the first d_v dims of that row, so one LDS tile of KV rows
 // feeds both contractions.
 //
-// Work decomposition.  A workgroup owns (request b, a chunk of 32-token tiles,
-// a group of up to 32*WH heads).  Its WH*WV waves each hold 32 heads:
-// wave (wh, wv) computes the scores of heads [32*wh, 32*wh+32) and the output
-// columns of V block range wv.  With WV > 1 the score tile is computed
-// redundantly by the WV waves of a head group (cheap at small head counts,
-// where the kernel is bound by HBM, not by the matrix cores).
+// Work decomposition.  A workgroup owns segments of (request b, a run of
+// 32-token tiles, a group of up to 32*WH heads): one chunk of a grid, or the
+// requests its range of the batch's tiles covers (the stream plan in
+// decode_device.h).  Its WH*WV waves each hold 32 heads: wave (wh, wv)
+// computes the scores of heads [32*wh, 32*wh+32) and the output columns of V
+// block range wv.  With WV > 1 the WV waves of a head group split the score
+// contraction's k-steps and sum their partial tiles through LDS.  Shares of
+// at most 16 heads per KV head run the 16-head tile of decode_attn16.hip.
 //
 // Per 32-token tile:
 //  * the KV rows (tile x d_qk bf16) land in an LDS ring slot through
@@ -31,8 +33,9 @@
 // with the exponentials of tile j-1 between its MFMAs, then updates the
 // output with tile j-1 while the VALU finds tile j's row max between the PV
 // MFMAs: the softmax runs while the matrix cores work.
-// A chunk writes normalised O and LSE (to the caller's output, or to the
-// split-KV workspace that splash_lse_merge then combines).
+// A segment writes normalised O and LSE to the caller's output, or a scaled
+// fp16 partial and its records to the split-KV workspace, which the merge
+// kernel (lse_merge.hip) then combines on the same stream.
 //
 // Pages cited: the weekinpapers page is "SPLASH: Switching Parallel Layouts of
 // Attention with Seamless Handoff for LLM Serving" (weekinpapers.com); the
