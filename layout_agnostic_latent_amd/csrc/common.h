@@ -55,7 +55,8 @@ struct DecodeArgs {
   int32_t grid_partial;
   // Stream mode (plan_target > 0): the batch's tiles cut into equal ranges
   // on the device (stream_plan_*), at most plan_target per head group;
-  // req_info[b] is request b's merge record (StreamRecord).
+  // req_info[b] is request b's merge record (stream_record: first and last
+  // range, slot of the first segment, kind).
   int32_t plan_target;
   int32_t plan_min_chunk;
   int32_t plan_header;       // tiles a segment start is counted as

@@ -88,7 +88,7 @@ __device__ __forceinline__ float max_across_halves(float x) {
 // output; a request cut by a range boundary leaves one partial per range it
 // touches, in slot w for the range's first segment and plan_target + w for
 // its last (so a uniform batch's partials are contiguous, by range).
-// Workgroup (0, 0, 0) writes each request's merge record (StreamRecord).
+// Workgroup (0, 0, 0) writes each request's merge record (stream_record).
 // All plan arithmetic is 32-bit: the host uses this plan only while every
 // virtual tile count fits in 31 bits.
 struct StreamPlan {
