@@ -1049,6 +1049,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
   // rows; stored directly, every instruction would touch 32 rows.  Each wave
   // instead writes its rows into its own LDS region (the ring is free once
   // every wave is past its last PV) and stores them back as whole 1-KiB runs.
+  // The stores are non-temporal: the rows go to memory now instead of sitting
+  // dirty in L2 until the write-back at the kernel's end.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float lr_tot = lr_run + __shfl_xor(lr_run, 32, 64);
   const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
@@ -1079,7 +1081,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
           const int e = (i * 64 + lane) * 4;
           const int row = e / ROWF, col = e % ROWF;
           const floatx4 v = *(const floatx4*)(stage + row * C::PITCH + col);
-          if (head0 + row < k_hi) *(floatx4*)(out_base + (int64_t)row * D_V + col0 + col) = v;
+          if (head0 + row < k_hi) __builtin_nontemporal_store(v, (floatx4*)(out_base + (int64_t)row * D_V + col0 + col));
         }
       } else {
         // Split-KV partial: the pass's ROWF columns of a row (one column
@@ -1109,7 +1111,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
             halfx8 h;
 #pragma unroll
             for (int k = 0; k < 8; ++k) h[k] = (_Float16)((k < 4 ? v0[k] : v1[k - 4]) * isc);
-            if (head0 + row < k_hi) *(halfx8*)(hbase + (int64_t)row * D_V + col0 + col) = h;
+            if (head0 + row < k_hi) __builtin_nontemporal_store(h, (halfx8*)(hbase + (int64_t)row * D_V + col0 + col));
           }
         } else {
 #pragma unroll
@@ -1121,7 +1123,7 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
             halfx8 h;
 #pragma unroll
             for (int k = 0; k < 8; ++k) h[k] = (_Float16)(k < 4 ? v0[k] : v1[k - 4]);
-            if (head0 + row < k_hi) *(halfx8*)(hbase + (int64_t)row * D_V + col0 + col) = h;
+            if (head0 + row < k_hi) __builtin_nontemporal_store(h, (halfx8*)(hbase + (int64_t)row * D_V + col0 + col));
           }
         }
       }
