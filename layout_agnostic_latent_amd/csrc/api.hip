@@ -322,7 +322,8 @@ int make_plan(const splash_desc* d, int32_t head_lo, int32_t head_hi, int32_t to
     // over equal sub-ranges of its tiles, and the merge combines every
     // sub-range.  One chunk (num_splits = 1) always runs unsplit.
     int64_t sub = forced > 1 && base * forced > 0 ? kNumCUs / (base * forced) : 1;
-    if (const char* env = getenv("SPLASH_CHUNK_WORKGROUPS")) {
+    const char* env = forced > 1 ? getenv("SPLASH_CHUNK_WORKGROUPS") : nullptr;
+    if (env) {
       const int v = atoi(env);
       if (v >= 1 && v <= 64) sub = v;
     }
@@ -456,7 +457,9 @@ int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, con
 
   const dim3 grid(p.stream ? p.target : p.grid_splits, p.stream ? 1 : desc->num_reqs, p.head_groups);
   if (p.grid_splits == 1) {
-    hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
+    hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) {
+      return launch_decode(p.variant, grid, a, stream, e0, e1);
+    });
     if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
     return SPLASH_OK;
   }
@@ -487,7 +490,9 @@ int decode_share(const splash_desc* desc, const void* q, const uint16_t* kv, con
   } else {
     a.grid_partial = 1;
   }
-  hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) { return launch_decode(p.variant, grid, a, stream, e0, e1); });
+  hipError_t e = timed(kDecode, [&](hipEvent_t e0, hipEvent_t e1) {
+    return launch_decode(p.variant, grid, a, stream, e0, e1);
+  });
   if (e != hipSuccess) return fail_hip(e, "decode_attn launch");
   e = timed(kMerge, [&](hipEvent_t e0, hipEvent_t e1) {
     return p.stream ? launch_split_merge_stream(a.part_o, a.part_l, sc_shift, a.req_info, (int32_t)rows, hs,

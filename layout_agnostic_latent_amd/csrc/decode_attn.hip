@@ -957,7 +957,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
     mask_tile(s, 0);
     m_run = tile_max(s);
     sprev = s;
-    if (3 < ntiles) dp = TBL ? tbl_plan(tbl[3], 3, 3 % C::NBUF) : dma_plan(t_begin + 3, 3 % C::NBUF, pages_of(t_begin + 3));
+    if (3 < ntiles)
+      dp = TBL ? tbl_plan(tbl[3], 3, 3 % C::NBUF) : dma_plan(t_begin + 3, 3 % C::NBUF, pages_of(t_begin + 3));
   }
 
   // Main loop, iteration j: wait for tile j and barrier (every wave is done
@@ -1081,7 +1082,8 @@ __global__ void __launch_bounds__(64 * WH * WV, 1) decode_attn_kernel(const Deco
           const int e = (i * 64 + lane) * 4;
           const int row = e / ROWF, col = e % ROWF;
           const floatx4 v = *(const floatx4*)(stage + row * C::PITCH + col);
-          if (head0 + row < k_hi) __builtin_nontemporal_store(v, (floatx4*)(out_base + (int64_t)row * D_V + col0 + col));
+          if (head0 + row < k_hi)
+            __builtin_nontemporal_store(v, (floatx4*)(out_base + (int64_t)row * D_V + col0 + col));
         }
       } else {
         // Split-KV partial: the pass's ROWF columns of a row (one column

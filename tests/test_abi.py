@@ -155,6 +155,9 @@ def test_plan_env_override(splash, monkeypatch):
     assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096)[0] == 5
     # an explicit num_splits in the descriptor wins
     assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_splits=3)[0] == 3
+    # one chunk always runs unsplit, whatever the workgroups-per-chunk override
+    monkeypatch.setenv("SPLASH_CHUNK_WORKGROUPS", "3")
+    assert sp.decode_plan(16, 128, 576, 512, 64, 64, 1024, 0.07, 0, 128, 0, 4096, num_splits=1)[:3:2] == (1, 0)
 
 
 def test_product_path_does_not_touch_the_oracle():
