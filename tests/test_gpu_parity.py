@@ -92,6 +92,29 @@ def test_owner_deterministic(owner):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_split_calls_on_two_streams(owner):
+    """Split-KV calls on two streams at once, over different data: each
+    stream has its own workspace, so neither call's merge reads the other's
+    partials (both shares cut into the same 256 ranges and partial slots)."""
+    c, t, (ro, rl) = owner
+    c2 = W.make_decode_case("owner2", 77, [4096] * 16, num_heads=128, d_qk=576, d_v=512, page_size=64,
+                            scale=W.LATENT_SCALE)
+    t2 = to_dev(c2)
+    ro2, rl2 = run_oracle(c2)
+    _print("case owner on two streams")
+    streams = [torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)]
+    outs = [torch.full((16, 128, 512), float("nan"), dtype=torch.float32, device=DEV) for _ in range(2)]
+    lses = [torch.full((16, 128), float("nan"), dtype=torch.float32, device=DEV) for _ in range(2)]
+    torch.cuda.synchronize()
+    for _ in range(4):
+        for k, (cc, tt) in enumerate(((c, t), (c2, t2))):
+            sp.decode_attn(tt["q"], tt["kv"], tt["bt"], tt["sl"], 0, 128, 0, 1 << 30, outs[k], lses[k],
+                           d_v=cc.d_v, scale=cc.scale, stream=streams[k])
+    torch.cuda.synchronize()
+    for k, (o, l) in enumerate(((ro, rl), (ro2, rl2))):
+        assert_close(outs[k].cpu().double().numpy(), lses[k].cpu().double().numpy(), o, l, what=f"stream {k}")
+
+
 def test_owner_request_subsets(owner):
     """DP-attention / DOP: each owner's call over its own requests equals the batch."""
     c, t, (ro, rl) = owner
