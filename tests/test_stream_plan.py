@@ -108,3 +108,27 @@ def test_uniform_batch_ranges_fall_on_request_boundaries():
     segments, records = plan([128] * 16, 12)
     assert all(len(s) == 1 and s[0][2] - s[0][1] == 8 for s in segments.values())
     assert all(kind == "parts" and len(parts) == 16 for kind, parts in records)
+
+
+@pytest.mark.parametrize("target", [128, 85, 16])
+def test_parts_in_range_order_and_no_slot_written_twice(target):
+    """Fewer ranges (wider head groups take 256 / groups of them): the parts
+    of a request come one per range, in range order, at the slots its record
+    names in that order, and no slot is written by two segments."""
+    rng = random.Random(target)
+    for _ in range(800):
+        tiles = [rng.choice([0, 1, 3, 17, 100, 1000, rng.randint(0, 5000)]) for _ in range(rng.randint(1, 70))]
+        if sum(tiles) == 0:
+            continue
+        segments, records = plan(tiles, 12, target)
+        slots, by_req = set(), {}
+        for w in sorted(segments):
+            segs = segments[w]
+            for k, (r, t0, t1, partial, slot) in enumerate(segs):
+                if partial:
+                    assert k == 0 or k == len(segs) - 1      # only a range's ends are cut
+                    assert slot not in slots
+                    slots.add(slot)
+                    by_req.setdefault(r, []).append(slot)
+        for r, (kind, parts) in enumerate(records):
+            assert by_req.get(r, []) == (parts if kind == "parts" else [])
