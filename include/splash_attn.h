@@ -75,7 +75,11 @@ typedef struct splash_desc {
                                 (env SPLASH_NUM_SPLITS overrides).  While num_reqs x chunks x head
                                 groups is below the CU count, each of two or more chunks is
                                 computed by several workgroups over equal sub-ranges, and the
-                                merge combines them all; 1 always runs unsplit */
+                                merge combines them all; 1 always runs unsplit.  Tuning
+                                overrides, read on the host at each call: SPLASH_CHUNK_WORKGROUPS
+                                (workgroups per forced chunk, 1..64), SPLASH_PLAN_HEADER (tiles a
+                                segment start counts as in the device plan, 0..64) and
+                                SPLASH_WG_HEADS (query heads per workgroup: 16, 32, 64 or 128) */
   float scale;               /* softmax scale applied to q.k, e.g. 1/sqrt(192) */
   int32_t num_kv_heads;      /* G latent KV heads per token (0 or 1: one); num_heads must be a multiple */
 } splash_desc;
