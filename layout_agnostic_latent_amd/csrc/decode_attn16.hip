@@ -389,12 +389,12 @@ __global__ void __launch_bounds__(256, 1) decode_attn16_kernel(const DecodeArgs 
 
   // ---- the workgroup's segments (as in the wider kernel) ----
   const bool stream = a.plan_target > 0;
-  StreamPlan sp{0, 0, 0, 0, 0};
+  StreamPlan sp{0, 0, 0, 0, 0, 0};
   if (stream) {
     sp = a.num_reqs <= 64 ? stream_plan_wave(a) : stream_plan_block<C::NTHREADS>(a, plan_lds);
     sp = StreamPlan{__builtin_amdgcn_readfirstlane(sp.A), __builtin_amdgcn_readfirstlane(sp.E),
                     __builtin_amdgcn_readfirstlane(sp.r), __builtin_amdgcn_readfirstlane(sp.V),
-                    __builtin_amdgcn_readfirstlane(sp.h)};
+                    __builtin_amdgcn_readfirstlane(sp.h), __builtin_amdgcn_readfirstlane(sp.n0)};
     if (sp.r < 0) return;
   }
   const int lo = max(a.tok_lo, 0);
@@ -405,8 +405,9 @@ __global__ void __launch_bounds__(256, 1) decode_attn16_kernel(const DecodeArgs 
     int64_t prow = 0;
     bool partial = false;
     if (stream) {
-      int nt = 0;
-      while (V < sp.E && r < a.num_reqs && (nt = request_tiles(a, r)) == 0) ++r;
+      int nt = k == 0 ? sp.n0 : 0;  // the first request's tiles come with the plan
+      if (k > 0)
+        while (V < sp.E && r < a.num_reqs && (nt = request_tiles(a, r)) == 0) ++r;
       const int R0 = V + sp.h;
       if (V >= sp.E || r >= a.num_reqs || R0 >= sp.E) break;
       const int s0 = max(sp.A, R0), s1 = min(sp.E, R0 + nt);

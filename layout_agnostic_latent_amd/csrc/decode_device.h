@@ -96,6 +96,7 @@ struct StreamPlan {
   int r;     // request whose run holds tile A (-1: nothing to do)
   int V;     // first virtual tile of request r's run
   int h;     // header tiles of every run
+  int n0;    // real tiles of request r (> 0), so the segment walk need not load it again
 };
 
 struct StreamCut {
@@ -155,18 +156,18 @@ __device__ StreamPlan stream_plan_wave(const DecodeArgs& a) {
   if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x < 64 && lane < a.num_reqs)
     a.req_info[lane] = stream_record(excl, incl, header, c, a.plan_target);
   const int w = blockIdx.x;
-  if (w >= c.N) return StreamPlan{0, 0, -1, 0, 0};
+  if (w >= c.N) return StreamPlan{0, 0, -1, 0, 0, 0};
   const int A = w * c.L, E = min(A + c.L, TV);  // the last range ends with the batch
   // the first run ending past A holds tile A (empty requests have no run)
   const unsigned long long bal = __ballot(lane < a.num_reqs && incl > A);
   const int r = __ffsll((long long)bal) - 1;
-  return StreamPlan{A, E, r, __builtin_amdgcn_readlane(excl, r), header};
+  return StreamPlan{A, E, r, __builtin_amdgcn_readlane(excl, r), header, __builtin_amdgcn_readlane(nt, r)};
 }
 
 // The same plan for batches of up to kPlanMaxReqs requests, by the
 // workgroup: thread t sums the runs of requests [t * per, t * per + per), a
 // wave scan and the waves' totals through LDS give every prefix.  `scratch`
-// (LDS, >= 3 NT / 64 + 2 ints) is free again on return.
+// (LDS, >= 3 NT / 64 + 3 ints) is free again on return.
 template <int NT>
 __device__ StreamPlan stream_plan_block(const DecodeArgs& a, int32_t* scratch) {
   constexpr int NWV = NT / 64;
@@ -187,8 +188,8 @@ __device__ StreamPlan stream_plan_block(const DecodeArgs& a, int32_t* scratch) {
     tmin = min(tmin, __shfl_xor(tmin, d, 64));
   }
   int* wsum = scratch;                // [NWV]
-  int* found = scratch + NWV;         // {r, V}
-  int* ext = scratch + NWV + 2;       // [NWV][2]: each wave's max and min
+  int* found = scratch + NWV;         // {r, V, tiles of r}
+  int* ext = scratch + NWV + 3;       // [NWV][2]: each wave's max and min
   if (lane == 0) {
     ext[2 * wave] = tmax;
     ext[2 * wave + 1] = tmin;
@@ -235,11 +236,12 @@ __device__ StreamPlan stream_plan_block(const DecodeArgs& a, int32_t* scratch) {
     if (active && v <= A && A < v + nv) {  // exactly one run holds tile A
       found[0] = r;
       found[1] = v;
+      found[2] = nv - header;
     }
     v += nv;
   }
   __syncthreads();
-  const StreamPlan p{A, E, active ? found[0] : -1, found[1], header};
+  const StreamPlan p{A, E, active ? found[0] : -1, found[1], header, found[2]};
   __syncthreads();
   return p;
 }
