@@ -453,7 +453,7 @@ def test_page16_range_starting_mid_tile(tok_lo):
         assert_close(go, gl, ro, rl, what=f"page 16, tok_lo {tok_lo}, splits {splits}")
 
 
-@pytest.mark.parametrize("ps", [16, 64, 256])
+@pytest.mark.parametrize("ps", [16, 32, 64, 128, 256])
 def test_head16_tile_pages_ranges_and_groups(ps):
     """Shares of at most 16 heads run on the 16x16x32 tile: page sizes 16 to
     256; a token range starting in the second half of a 32-token tile with
@@ -492,6 +492,27 @@ def test_head16_tile_rescale():
         go, gl = run_decode(c, head_lo=32, head_hi=48, num_splits=splits)
         ro, rl = run_oracle(c, head_lo=32, head_hi=48)
         assert_close(go, gl, ro, rl, what=f"16-head tile, growing scores, splits {splits}")
+
+
+@pytest.mark.parametrize("ps", [16, 32, 128, 256])
+def test_128_head_tile_page_sizes(ps):
+    """The 128-head tile (four waves, the tile-address table) on every page
+    size: each wave's 8-row group of a tile lies in one page, whose offset the
+    table holds; ranges starting mid-tile and mid-page, with the entries
+    before them -1; unsplit, forced and planned splits."""
+    tok_lo = 16 + ps
+    c = W.make_decode_case("p128h", 90 + ps, [1500, 40, 700, 2], num_heads=128, d_qk=576, d_v=512,
+                           page_size=ps, scale=W.LATENT_SCALE, tok_lo=tok_lo, tok_hi=1400,
+                           live_only_in_range=True, extra_pages=2)
+    bt = c.block_table.copy()
+    bt[:, :tok_lo // ps] = -1
+    c2 = W.DecodeCase(**{**c.__dict__, "block_table": bt})
+    t = to_dev(c2)
+    ro, rl = run_oracle(c2)
+    for splits in (0, 1, 3):
+        _print(f"case 128-head tile ps={ps} splits={splits}")
+        go, gl = run_decode(c2, t, num_splits=splits)
+        assert_close(go, gl, ro, rl, what=f"128-head tile, page {ps}, splits {splits}")
 
 
 @pytest.mark.parametrize("ps", [16, 32, 128, 256])
