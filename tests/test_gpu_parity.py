@@ -413,6 +413,21 @@ def test_one_long_request_many_chunks():
     assert_close(go, gl, ro, rl, what="long request")
 
 
+@pytest.mark.parametrize("n_tok,ps,heads", [(40000, 64, (0, 128)), (70000, 16, (0, 128)), (40000, 64, (0, 32)),
+                                             (40000, 64, (0, 64)), (70000, 16, (16, 32))])
+def test_unsplit_long_chunks(n_tok, ps, heads):
+    """One chunk per request (num_splits = 1) longer than the 128-head tile's
+    address table holds: the page ids come from LDS (up to 4,096 pages) or
+    through the scalar cache (more, and in the 64- and 32-head variants,
+    whose LDS holds the score exchange); the 16-head tile likewise."""
+    c = W.make_decode_case("longchunk", 95 + ps, [n_tok, 333], num_heads=128, d_qk=576, d_v=512, page_size=ps,
+                           scale=W.LATENT_SCALE, head_lo=heads[0], head_hi=heads[1])
+    _print(f"case unsplit long chunk tokens={n_tok} page={ps} heads={heads}")
+    go, gl = run_decode(c, num_splits=1)
+    ro, rl = run_oracle(c)
+    assert_close(go, gl, ro, rl, what=f"unsplit {n_tok} tokens, page {ps}, heads {heads}")
+
+
 def test_ragged_edges():
     """Zero-length, one-token, unaligned and page-straddling requests in one batch."""
     lens = [0, 1, 31, 32, 33, 63, 64, 65, 200, 1000]
